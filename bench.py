@@ -1,0 +1,183 @@
+"""Benchmark: one training step of the packed varlen width-4 depthwise causal
+conv1d + SiLU (forward kernel, then the backward main + reduce kernels) on
+the headline workload (S = 65536 tokens, C = 4096 channels, 22 lognormal
+documents, FP32 weight and bias, "bf16" SiLU' policy), inputs resident in
+HBM, timed with HIP events on the stream the library launches on.
+
+Prints one JSON line.  `value` is the step's algorithmic HBM traffic
+(forward 4 B + backward 6 B per token-channel, plus parameters) divided by
+the step time, in GB/s; per-direction GB/s, Mtokens/s and fractions of the
+8 TB/s MI355X HBM peak are alongside.  `cpu_baseline` times the FP64 CPU
+oracle on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fwd/bwd HBM GB/s + Mtokens/s, S=64K C=4096 packed; % of HBM roofline"
+HBM_PEAK_GBS = 8000.0
+WORKLOAD = "headline"
+CPU_SAMPLE_CHANNELS = 2048
+
+
+def algorithmic_bytes(wl, direction):
+    """Minimum HBM bytes of one call: activations plus parameters and cu_seqlens."""
+    S, C = wl.S, wl.C
+    pw = C * 4 * (4 if wl.w_dtype == "f32" else 2)
+    pb = 0 if wl.b is None else C * (4 if wl.b_dtype == "f32" else 2)
+    cu = 4 * wl.cu.size
+    if direction == "fwd":
+        return 4 * S * C + pw + pb + cu            # read x, write y
+    # read x and dy, write dx; write dweight and dbias (FP32 here)
+    return 6 * S * C + pw + pb + cu + C * 4 * 4 + (0 if wl.b is None else C * 4)
+
+
+def gpu_leg(wl, policy, steps, warmup):
+    import torch
+    import varlen_depthwise_causal_amd as vdc
+
+    dev = torch.device("cuda:0")
+
+    def bf16(a):
+        import numpy as np
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, dy = bf16(wl.x), bf16(wl.dy)
+    w = torch.from_numpy(wl.w).to(dev) if wl.w_dtype == "f32" else bf16(wl.w)
+    b = None
+    if wl.b is not None:
+        b = torch.from_numpy(wl.b).to(dev) if wl.b_dtype == "f32" else bf16(wl.b)
+    cu = torch.from_numpy(wl.cu).to(dev)
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    dw = torch.empty((wl.C, 4), dtype=torch.float32, device=dev)
+    db = torch.empty((wl.C,), dtype=torch.float32, device=dev) if b is not None else None
+    ws = torch.empty(max(vdc.workspace_bytes("bwd", wl.S, wl.C), 1), dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        vdc.conv1d_fwd(x, w, cu, bias=b, out=y)
+        if ev:
+            ev[1].record()
+        vdc.conv1d_bwd(x, w, cu, dy, bias=b, silu_grad_preactivation=policy, workspace=ws,
+                       dx=dx, dweight=dw, dbias=db)
+        if ev:
+            ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
+    bwd_ms = [e[1].elapsed_time(e[2]) for e in events]
+    return {"wall_s": wall, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+            "plan_fwd": vdc.conv1d_plan("fwd", wl.S, wl.C, policy),
+            "plan_bwd": vdc.conv1d_plan("bwd", wl.S, wl.C, policy)}
+
+
+def cpu_leg(wl, policy):
+    """The FP64 oracle, single-threaded, on every token of a channel sample."""
+    import numpy as np
+    import oracle
+
+    cols = np.arange(CPU_SAMPLE_CHANNELS)
+    x = oracle.decode_bf16(wl.x[:, cols])
+    dy = oracle.decode_bf16(wl.dy[:, cols])
+    w = oracle.decode_param(wl.w, wl.w_dtype)[cols]
+    b = oracle.decode_param(wl.b, wl.b_dtype)[cols] if wl.b is not None else None
+    t0 = time.perf_counter()
+    oracle.forward(x, w, b, wl.cu, want=("y",))
+    oracle.backward(x, w, b, wl.cu, dy, policy, want=("dx", "dw", "db"))
+    dt = time.perf_counter() - t0
+    elems = wl.S * len(cols)
+    return {"value": round(10 * elems / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "all %d tokens x %d of %d channels (channels are independent), "
+                      "forward + backward, FP64 C oracle, one thread, %.1f s"
+                      % (wl.S, len(cols), wl.C, dt),
+            "mtokens_per_s_full_width": round(elems / wl.C / dt / 1e6, 5)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--policy", default="bf16", choices=["bf16", "fp32"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU only (no multi-GPU sharding is built); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    from varlen_depthwise_causal_amd import workloads as W
+    wl = W.make(WORKLOAD, workers=16)
+    g = gpu_leg(wl, args.policy, args.steps, args.warmup)
+
+    fwd_ms = statistics.mean(g["fwd_ms"])
+    bwd_ms = statistics.mean(g["bwd_ms"])
+    step_ms = g["wall_s"] * 1e3 / args.steps
+    fb, bb = algorithmic_bytes(wl, "fwd"), algorithmic_bytes(wl, "bwd")
+    fwd_gbs = fb / (fwd_ms * 1e-3) / 1e9
+    bwd_gbs = bb / (bwd_ms * 1e-3) / 1e9
+    step_gbs = (fb + bb) / (step_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(step_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "%s: S=%d C=%d, %d packed documents (lognormal lengths), "
+                               "weight %s, bias %s, silu_grad_preactivation=%s"
+                               % (WORKLOAD, wl.S, wl.C, wl.num_docs, wl.w_dtype, wl.b_dtype,
+                                  args.policy),
+                   "S": wl.S, "C": wl.C, "docs": wl.num_docs, "policy": args.policy},
+        "step_frac_of_hbm_peak": round(step_gbs / HBM_PEAK_GBS, 4),
+        "step_mtokens_per_s": round(wl.S / (step_ms * 1e-3) / 1e6, 3),
+        "fwd": {"ms": round(fwd_ms, 4), "ms_median": round(statistics.median(g["fwd_ms"]), 4),
+                "GB_s": round(fwd_gbs, 2), "frac_of_peak": round(fwd_gbs / HBM_PEAK_GBS, 4),
+                "mtokens_per_s": round(wl.S / (fwd_ms * 1e-3) / 1e6, 3),
+                "algorithmic_bytes": fb, "plan": g["plan_fwd"]},
+        "bwd": {"ms": round(bwd_ms, 4), "ms_median": round(statistics.median(g["bwd_ms"]), 4),
+                "GB_s": round(bwd_gbs, 2), "frac_of_peak": round(bwd_gbs / HBM_PEAK_GBS, 4),
+                "mtokens_per_s": round(wl.S / (bwd_ms * 1e-3) / 1e6, 3),
+                "algorithmic_bytes": bb, "plan": g["plan_bwd"],
+                "partial_bytes": 2 * g["plan_bwd"]["bands"] * 5 * wl.C * g["plan_bwd"]["acc_bytes"]},
+        "roofline": {"kernel": "conv1d_bwd: bwd_main_kernel + bwd_reduce_kernel (one call)",
+                     "bound": "hbm", "achieved": round(bwd_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(bwd_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "roofline_fwd": {"kernel": "fwd_kernel", "bound": "hbm", "achieved": round(fwd_gbs, 2),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(fwd_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_leg(wl, args.policy)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

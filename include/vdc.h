@@ -1,0 +1,189 @@
+/*
+ * vdc.h - packed variable-length width-4 depthwise causal convolution
+ * followed by SiLU, training forward and backward, on AMD Instinct MI355X
+ * (gfx950).  C ABI of libvdc.so.
+ *
+ * The operation is the one documented on the pages of
+ * flashinfer.cake_causal_conv1d_train:
+ *   [F] cake_causal_conv1d_train_forward  (Parameters, Returns)
+ *   [B] cake_causal_conv1d_train_backward (Description, Parameters, Returns)
+ *
+ * Many documents are packed back to back into one [S, C] activation tensor;
+ * int32 cu_seqlens[0..num_docs] holds the prefix sums of their lengths
+ * (cu_seqlens[0] = 0, cu_seqlens[num_docs] = S, a repeated value is an empty
+ * document).  For token t in a document starting at s, channel c:
+ *
+ *   p[t,c]  = sum_{k=0..3, t-3+k >= s} w[c,k] * x[t-3+k,c]  (+ b[c])
+ *   y[t,c]  = bf16(SiLU(p[t,c]))                                   [F] Returns
+ *
+ * w[c,3] multiplies the current token and w[c,0] the token three back; the
+ * bias is added after the four taps ([F] Parameters).  The backward
+ * recomputes p in FP32 and forms dpre = dy * SiLU'(z), where z is p rounded
+ * to BF16 (policy VDC_SILU_GRAD_BF16, the default) or p itself
+ * (VDC_SILU_GRAD_FP32) ([B] Description, Parameters silu_grad_preactivation).
+ * Then, with e the end of t's document ([B] Returns):
+ *
+ *   dx[t,c]      = bf16(sum_{k, t+3-k < e} w[c,k] * dpre[t+3-k,c])
+ *   dweight[c,k] = sum_t dpre[t,c] * x[t-3+k,c]   (taps inside the document)
+ *   dbias[c]     = sum_t dpre[t,c]
+ *
+ * dweight and dbias are reduced in a fixed order that depends only on
+ * (S, C, policy), so they are bitwise reproducible for a given (S, C, device)
+ * and route ([B] Returns, Description).
+ *
+ * General rules for every entry point below:
+ *  - Pointers to tensors are DEVICE pointers; sizes are element counts.
+ *    Tensors are dense and row-major; x / dy / y / dx are [S][C] bf16 and
+ *    must be 16-byte aligned; weight is [C][4] and bias [C], both 16-byte
+ *    aligned; dweight [C][4] and
+ *    dbias [C] are 4-byte (FP32) or 2-byte (BF16) aligned; each is FP32 or
+ *    BF16 as its dtype argument says; cu_seqlens is int32 [num_docs + 1].
+ *  - The caller owns every buffer.  The library allocates nothing, frees
+ *    nothing, keeps no per-call state, never synchronizes, and never reads
+ *    device memory on the host (in particular not cu_seqlens, whose
+ *    well-formedness is the caller's precondition, [F] Parameters
+ *    cu_seqlens; for malformed values the kernels stay inside their buffers
+ *    and the results are unspecified).
+ *  - Work is only enqueued on `stream` (0 = the null stream).  Calls are
+ *    safe to capture into a HIP graph once the workspace exists.
+ *  - Every argument is validated on the host before anything is enqueued;
+ *    on a non-zero status nothing was enqueued and no output was touched.
+ *  - Two calls that may run concurrently need two workspaces.
+ */
+#ifndef VDC_H
+#define VDC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtype codes of weight / bias / dweight / dbias ([F] Parameters weight,
+ * bias; [B] Parameters dweight, dbias). */
+enum vdc_dtype {
+    VDC_F32 = 0,
+    VDC_BF16 = 1
+};
+
+/* Where SiLU' is evaluated ([B] Parameters, silu_grad_preactivation). */
+enum vdc_silu_grad {
+    VDC_SILU_GRAD_BF16 = 0, /* at the BF16-rounded FP32 preactivation      */
+    VDC_SILU_GRAD_FP32 = 1  /* at the FP32 preactivation; FP64 reduction   */
+};
+
+/* Direction argument of workspace_bytes. */
+enum vdc_direction {
+    VDC_FWD = 0,
+    VDC_BWD = 1
+};
+
+/* Status codes returned by the entry points. */
+enum vdc_status {
+    VDC_OK = 0,
+    VDC_EINVAL = 1,     /* bad size, missing pointer, overlapping buffers  */
+    VDC_EDTYPE = 2,     /* unknown dtype or policy code                    */
+    VDC_EALIGN = 3,     /* a tensor pointer is not aligned as required     */
+    VDC_EWORKSPACE = 4, /* workspace missing or smaller than required      */
+    VDC_ENOBIAS = 5,    /* dbias requested without a bias                  */
+    VDC_EHIP = 6        /* the HIP runtime refused a launch                */
+};
+
+/*
+ * workspace_bytes - bytes of workspace a call needs.
+ *
+ * [F] Parameters workspace and [B] Parameters workspace: one size that
+ * serves every route of the direction.  VDC_FWD: the forward keeps no
+ * counters and needs no workspace, so the answer is 0 (conv1d_fwd accepts
+ * workspace = NULL).  VDC_BWD: room for the per-band FP32 / FP64 partial
+ * rows of dweight and dbias for every policy, at this (S, C); the backward
+ * writes every byte it later reads, so the buffer needs no zeroing
+ * ([B] Parameters workspace).
+ *
+ * direction: VDC_FWD or VDC_BWD.  S >= 0 tokens, C > 0 channels (a multiple
+ * of 8).  Returns 0 for invalid arguments (and for every valid forward).
+ */
+size_t workspace_bytes(int direction, int64_t S, int64_t C);
+
+/*
+ * conv1d_fwd - training forward ([F] Returns).
+ *
+ * x          bf16 [S][C], 16-byte aligned, C a multiple of 8 ([F] Parameters x).
+ * weight     [C][4] of dtype w_dtype (VDC_F32 / VDC_BF16) ([F] Parameters weight).
+ * bias       [C] of dtype b_dtype, or NULL for no bias; b_dtype is ignored
+ *            when bias is NULL ([F] Parameters bias).
+ * cu_seqlens int32 [num_docs + 1] device prefix sums; num_docs >= 1 when
+ *            S > 0 ([F] Parameters cu_seqlens).
+ * y          bf16 [S][C] output, 16-byte aligned, must not overlap x
+ *            ([F] Parameters out).
+ * workspace, ws_bytes: may be NULL / 0 (workspace_bytes(VDC_FWD) is 0).
+ * stream     the HIP stream the kernel is enqueued on.
+ *
+ * S == 0 enqueues nothing ([F] Returns).  Returns a vdc_status.
+ */
+int conv1d_fwd(const void *x, const void *weight, int w_dtype,
+               const void *bias, int b_dtype,
+               const int32_t *cu_seqlens, int64_t num_docs,
+               int64_t S, int64_t C,
+               void *y, void *workspace, size_t ws_bytes,
+               hipStream_t stream);
+
+/*
+ * conv1d_bwd - training backward ([B] Description, Returns).
+ *
+ * x, weight, w_dtype, bias, b_dtype, cu_seqlens, num_docs, S, C: the
+ *            forward's inputs, same contracts as conv1d_fwd
+ *            ([B] Parameters x, weight, cu_seqlens, bias).
+ * dy         bf16 [S][C] gradient of y, 16-byte aligned ([B] Parameters dy).
+ * policy     VDC_SILU_GRAD_BF16 or VDC_SILU_GRAD_FP32.
+ * dx         bf16 [S][C] output, 16-byte aligned; must not overlap x or dy.
+ * dweight    [C][4] output of dtype dw_dtype (VDC_F32 / VDC_BF16).
+ * dbias      [C] output of dtype db_dtype, or NULL; non-NULL needs a bias
+ *            (VDC_ENOBIAS otherwise) ([B] Parameters dbias).
+ * workspace  at least workspace_bytes(VDC_BWD, S, C) bytes, 16-byte aligned,
+ *            contents irrelevant; must not overlap any other argument.
+ *
+ * Two launches are enqueued in stream order: the main kernel writes dx and
+ * one partial row of dweight / dbias per band of tokens into the workspace,
+ * and the reduce kernel sums the rows in a fixed order (FP32 under
+ * VDC_SILU_GRAD_BF16, FP64 under VDC_SILU_GRAD_FP32) and rounds once to the
+ * output dtype ([B] Description).  S == 0 launches neither kernel: dweight
+ * (and dbias) are set to zero with hipMemsetAsync, or, if the stream is
+ * being captured into a graph, with a small fill kernel ([B] Returns).
+ * Returns a vdc_status.
+ */
+int conv1d_bwd(const void *x, const void *weight, int w_dtype,
+               const void *bias, int b_dtype,
+               const int32_t *cu_seqlens, int64_t num_docs,
+               const void *dy, int64_t S, int64_t C, int policy,
+               void *dx, void *dweight, int dw_dtype,
+               void *dbias, int db_dtype,
+               void *workspace, size_t ws_bytes,
+               hipStream_t stream);
+
+/* conv1d_status_string - static English text of a vdc_status code. */
+const char *conv1d_status_string(int status);
+
+/*
+ * conv1d_plan - the launch plan a call with these sizes would use
+ * (introspection for tests and benchmarks; enqueues nothing).
+ * Fills out[0..7] = { rows per band, bands (= partial rows of the
+ * backward), lanes (bands * C/8), main-kernel workgroups, threads per
+ * workgroup, partial element bytes (0 forward, 4 or 8 backward),
+ * reduce-kernel workgroups, reduce chunks }.  Returns a vdc_status.
+ */
+int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int64_t out[8]);
+
+/* conv1d_launch_count - kernels this process has launched through the
+ * library so far (a diagnostic counter, e.g. to check that S == 0
+ * launches nothing). */
+uint64_t conv1d_launch_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VDC_H */

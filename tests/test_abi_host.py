@@ -1,0 +1,174 @@
+"""Host-only checks of the C ABI (no GPU needed, nothing is ever enqueued).
+
+Every call here fails validation before the library touches the HIP
+runtime; the pointers are fake device addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vdc.h")
+
+OK, EINVAL, EDTYPE, EALIGN, EWORKSPACE, ENOBIAS, EHIP = range(7)
+F32, BF16 = 0, 1
+FWD, BWD = 0, 1
+
+A = 0x7F0000000000          # fake, 16-byte aligned device addresses, far apart
+B = 0x7F1000000000
+W = 0x7F2000000000
+BIAS = 0x7F3000000000
+CU = 0x7F4000000000
+DY = 0x7F5000000000
+DX = 0x7F6000000000
+DW = 0x7F7000000000
+DB = 0x7F8000000000
+WS = 0x7F9000000000
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from varlen_depthwise_causal_amd import _build, _lib
+    if not os.path.exists(_build.LIBRARY):
+        _build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("conv1d_fwd", "conv1d_bwd", "workspace_bytes", "conv1d_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(lib._name)
+    for n in declared_functions():
+        assert hasattr(raw, n), "libvdc.so does not export %s" % n
+
+
+def fwd(lib, x=A, w=W, wd=F32, b=BIAS, bd=F32, cu=CU, D=3, S=1000, C=64, y=B, ws=None, wsn=0):
+    return lib.conv1d_fwd(x, w, wd, b, bd, cu, D, S, C, y, ws, wsn, None)
+
+
+def bwd(lib, x=A, w=W, wd=F32, b=BIAS, bd=F32, cu=CU, D=3, dy=DY, S=1000, C=64, pol=0,
+        dx=DX, dw=DW, dwd=F32, db=DB, dbd=F32, ws=WS, wsn=None):
+    if wsn is None:
+        wsn = lib.workspace_bytes(BWD, S, C)
+    return lib.conv1d_bwd(x, w, wd, b, bd, cu, D, dy, S, C, pol, dx, dw, dwd, db, dbd, ws, wsn, None)
+
+
+def test_forward_validation(lib):
+    n0 = lib.conv1d_launch_count()
+    assert fwd(lib, C=0) == EINVAL
+    assert fwd(lib, C=12) == EINVAL                     # not a multiple of 8
+    assert fwd(lib, C=(1 << 20) + 8) == EINVAL
+    assert fwd(lib, S=-1) == EINVAL
+    assert fwd(lib, S=1 << 31) == EINVAL
+    assert fwd(lib, D=0) == EINVAL                      # S > 0 needs a document
+    assert fwd(lib, D=-2) == EINVAL
+    assert fwd(lib, wd=2) == EDTYPE
+    assert fwd(lib, bd=9) == EDTYPE
+    assert fwd(lib, x=None) == EINVAL
+    assert fwd(lib, w=None) == EINVAL
+    assert fwd(lib, cu=None) == EINVAL
+    assert fwd(lib, y=None) == EINVAL
+    assert fwd(lib, x=A + 8) == EALIGN
+    assert fwd(lib, y=B + 2) == EALIGN
+    assert fwd(lib, w=W + 4) == EALIGN
+    assert fwd(lib, b=BIAS + 4) == EALIGN
+    assert fwd(lib, y=A) == EINVAL                      # in place
+    assert fwd(lib, y=A + 1000 * 64 * 2 - 16) == EINVAL  # partial overlap
+    assert fwd(lib, y=W) == EINVAL                      # output over the weights
+    assert lib.conv1d_launch_count() == n0
+
+
+def test_forward_zero_tokens_enqueues_nothing(lib):
+    n0 = lib.conv1d_launch_count()
+    assert fwd(lib, S=0, D=0, x=None, y=None, cu=None) == OK
+    assert fwd(lib, S=0, D=4) == OK
+    assert lib.conv1d_launch_count() == n0
+
+
+def test_backward_validation(lib):
+    n0 = lib.conv1d_launch_count()
+    need = lib.workspace_bytes(BWD, 1000, 64)
+    assert need > 0
+    assert bwd(lib, C=20) == EINVAL
+    assert bwd(lib, pol=2) == EDTYPE
+    assert bwd(lib, wd=3) == EDTYPE
+    assert bwd(lib, dwd=3) == EDTYPE
+    assert bwd(lib, dbd=-1) == EDTYPE
+    assert bwd(lib, b=None) == ENOBIAS                  # dbias needs a bias
+    assert bwd(lib, dw=None) == EINVAL
+    assert bwd(lib, dx=None) == EINVAL
+    assert bwd(lib, dy=None) == EINVAL
+    assert bwd(lib, ws=None) == EWORKSPACE
+    assert bwd(lib, wsn=need - 1) == EWORKSPACE
+    assert bwd(lib, ws=WS + 8) == EALIGN
+    assert bwd(lib, dx=DX + 2) == EALIGN
+    assert bwd(lib, dw=DW + 2) == EALIGN                # FP32 dweight: 4-byte aligned
+    assert bwd(lib, dy=DY + 4) == EALIGN
+    assert bwd(lib, dx=DY) == EINVAL                    # dx over dy
+    assert bwd(lib, dx=A) == EINVAL                     # dx over x
+    assert bwd(lib, ws=DX + 64) == EINVAL               # workspace over dx
+    assert bwd(lib, dw=DB) == EINVAL                    # dweight over dbias
+    assert bwd(lib, db=W) == EINVAL                     # dbias over the weights
+    assert lib.conv1d_launch_count() == n0
+
+
+def test_backward_bf16_gradients_alignment(lib):
+    # BF16 dweight only needs 2-byte alignment: the call passes validation up
+    # to a later failing check (here: a too small workspace).
+    assert bwd(lib, dw=DW + 2, dwd=BF16, wsn=1) == EWORKSPACE
+
+
+def test_workspace_bytes(lib):
+    assert lib.workspace_bytes(FWD, 65536, 4096) == 0
+    assert lib.workspace_bytes(BWD, 0, 64) == 0
+    assert lib.workspace_bytes(BWD, 100, 12) == 0          # invalid C
+    assert lib.workspace_bytes(7, 100, 64) == 0
+    for S, C in ((1000, 64), (65536, 4096), (262144, 520), (131072, 8192), (1, 8)):
+        n = lib.workspace_bytes(BWD, S, C)
+        out = (ctypes.c_int64 * 8)()
+        assert lib.conv1d_plan(BWD, S, C, 1, out) == OK
+        rows, bands = out[0], out[1]
+        assert bands == -(-S // rows)
+        assert n == bands * 5 * C * 8                        # FP64 partials of every band
+        assert lib.conv1d_plan(BWD, S, C, 0, out) == OK
+        assert out[5] == 4 and n >= out[1] * 5 * C * 4
+
+
+def test_plans_depend_on_shape_only(lib):
+    for d in (FWD, BWD):
+        for S, C in ((65536, 4096), (262144, 520), (1000, 64)):
+            a, b = (ctypes.c_int64 * 8)(), (ctypes.c_int64 * 8)()
+            assert lib.conv1d_plan(d, S, C, 0, a) == OK
+            assert lib.conv1d_plan(d, S, C, 0, b) == OK
+            assert list(a) == list(b)
+            rows, bands, lanes, blocks, threads = a[0], a[1], a[2], a[3], a[4]
+            assert rows % 8 == 0 and rows >= 16
+            assert lanes == bands * (C // 8) and blocks * threads >= lanes
+            # a wave's span of rows stays far inside 32-bit byte offsets
+            span = (-(-64 // (C // 8)) + 1) * rows + 8
+            assert span * C * 2 < 2 ** 31
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert len(lib.conv1d_status_string(s)) > 0
+    assert lib.conv1d_status_string(99) == b"unknown status"
+
+
+def test_python_binding_refuses_without_library(tmp_path):
+    from varlen_depthwise_causal_amd import _lib
+    with pytest.raises(ImportError):
+        _lib.load(str(tmp_path / "missing.so"))

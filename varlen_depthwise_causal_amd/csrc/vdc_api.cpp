@@ -1,0 +1,272 @@
+// Host side of libvdc.so: argument validation, launch planning and the
+// C entry points declared in include/vdc.h.
+//
+// Nothing here allocates device memory, synchronizes, or reads device
+// memory: cu_seqlens is only passed through to the kernels (documentation
+// of flashinfer.cake_causal_conv1d_train_forward, Parameters cu_seqlens).
+
+#include "vdc.h"
+
+#include <atomic>
+#include <stdint.h>
+
+#include "vdc_internal.h"
+
+namespace vdc {
+namespace {
+
+std::atomic<uint64_t> g_launches{0};
+
+constexpr int64_t kMaxC = int64_t(1) << 20;
+constexpr int64_t kMaxS = (int64_t(1) << 31) - 1;
+// Lanes that keep the whole chip busy at the occupancy these kernels reach
+// (256 CUs x 8 wave64).
+constexpr int64_t kFillLanes = 256 * 8 * 64;
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+bool valid_dtype(int d) { return d == VDC_F32 || d == VDC_BF16; }
+size_t dtype_bytes(int d) { return d == VDC_BF16 ? 2 : 4; }
+
+// Largest span, in rows, one wave can touch: the bands of its 64 lanes
+// plus the halos.  Offsets inside that span must stay below 2^31 bytes.
+int64_t wave_span_rows(int64_t nvec, int64_t rows) {
+  return (ceil_div(64, nvec) + 1) * rows + 8;
+}
+
+// Tokens per band.  Forward: 64 (halo re-read 3/64 of x), fewer when the
+// problem is too small to fill the chip.  Backward: 256, more for large
+// problems (fewer partial rows) and fewer for small ones.  A function of
+// (direction, S, C) only.
+int32_t pick_rows(int dir, int64_t S, int64_t C) {
+  const int64_t nvec = C / kVec;
+  int64_t rows = dir == VDC_FWD ? 64 : 256;
+  const int64_t lo = 16;
+  auto lanes = [&](int64_t r) { return ceil_div(S, r) * nvec; };
+  while (rows > lo && lanes(rows) < kFillLanes) rows /= 2;
+  if (dir == VDC_BWD)
+    while (rows < 1024 && lanes(rows * 2) >= 2 * kFillLanes) rows *= 2;
+  while (rows > lo && wave_span_rows(nvec, rows) * C * 2 >= (int64_t(1) << 31)) rows /= 2;
+  return (int32_t)rows;
+}
+
+Plan make_plan(int dir, int64_t S, int64_t C, int policy) {
+  Plan p{};
+  p.rows = pick_rows(dir, S, C);
+  p.bands = (int32_t)ceil_div(S, p.rows);
+  p.lanes = (int64_t)p.bands * (C / kVec);
+  p.blocks = (int32_t)ceil_div(p.lanes, kBlock);
+  p.acc_bytes = dir == VDC_FWD ? 0 : (policy == VDC_SILU_GRAD_FP32 ? 8 : 4);
+  p.red_blocks = dir == VDC_FWD ? 0 : (int32_t)ceil_div(5 * C, kRedOut);
+  p.red_rows = dir == VDC_FWD ? 0 : (int32_t)ceil_div(p.bands, kRedChunks);
+  return p;
+}
+
+int check_sizes(int64_t S, int64_t C, int64_t num_docs) {
+  if (C <= 0 || C % kVec != 0 || C > kMaxC) return VDC_EINVAL;
+  if (S < 0 || S > kMaxS) return VDC_EINVAL;
+  if (num_docs < 0 || num_docs > kMaxS - 1) return VDC_EINVAL;
+  if (S > 0 && num_docs < 1) return VDC_EINVAL;
+  // The planner must find a band size whose wave span fits 32-bit offsets.
+  if (wave_span_rows(C / kVec, 16) * C * 2 >= (int64_t(1) << 31)) return VDC_EINVAL;
+  return VDC_OK;
+}
+
+}  // namespace
+}  // namespace vdc
+
+using namespace vdc;
+
+extern "C" size_t workspace_bytes(int direction, int64_t S, int64_t C) {
+  if (direction != VDC_FWD && direction != VDC_BWD) return 0;
+  if (check_sizes(S, C, S > 0 ? 1 : 0) != VDC_OK) return 0;
+  if (direction == VDC_FWD || S == 0) return 0;
+  // Largest partial element over the policies (FP64 under the fp32 policy).
+  const Plan p = make_plan(VDC_BWD, S, C, VDC_SILU_GRAD_FP32);
+  return (size_t)p.bands * 5 * (size_t)C * 8;
+}
+
+extern "C" int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int64_t out[8]) {
+  if (!out) return VDC_EINVAL;
+  if (direction != VDC_FWD && direction != VDC_BWD) return VDC_EINVAL;
+  if (direction == VDC_BWD && policy != VDC_SILU_GRAD_BF16 && policy != VDC_SILU_GRAD_FP32)
+    return VDC_EDTYPE;
+  int rc = check_sizes(S, C, S > 0 ? 1 : 0);
+  if (rc) return rc;
+  const Plan p = make_plan(direction, S, C, policy);
+  out[0] = p.rows;
+  out[1] = p.bands;
+  out[2] = p.lanes;
+  out[3] = p.blocks;
+  out[4] = kBlock;
+  out[5] = p.acc_bytes;
+  out[6] = p.red_blocks;
+  out[7] = kRedChunks;
+  return VDC_OK;
+}
+
+extern "C" int conv1d_fwd(const void* x, const void* weight, int w_dtype, const void* bias,
+                          int b_dtype, const int32_t* cu_seqlens, int64_t num_docs, int64_t S,
+                          int64_t C, void* y, void* workspace, size_t ws_bytes,
+                          hipStream_t stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  int rc = check_sizes(S, C, num_docs);
+  if (rc) return rc;
+  if (!valid_dtype(w_dtype)) return VDC_EDTYPE;
+  if (bias && !valid_dtype(b_dtype)) return VDC_EDTYPE;
+  if (S == 0) return VDC_OK;  // nothing to compute, nothing enqueued
+  if (!x || !weight || !cu_seqlens || !y) return VDC_EINVAL;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(weight, 16) || (bias && !aligned(bias, 16)))
+    return VDC_EALIGN;
+  const size_t act = (size_t)S * (size_t)C * 2;
+  if (overlaps(x, act, y, act)) return VDC_EINVAL;
+  if (overlaps(y, act, weight, (size_t)C * 4 * dtype_bytes(w_dtype))) return VDC_EINVAL;
+  if (bias && overlaps(y, act, bias, (size_t)C * dtype_bytes(b_dtype))) return VDC_EINVAL;
+  if (overlaps(y, act, cu_seqlens, (size_t)(num_docs + 1) * 4)) return VDC_EINVAL;
+
+  const Plan plan = make_plan(VDC_FWD, S, C, 0);
+  FwdArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.y = static_cast<uint16_t*>(y);
+  a.w = weight;
+  a.b = bias;
+  a.cu = cu_seqlens;
+  a.num_docs = (int32_t)num_docs;
+  a.w_bf16 = w_dtype == VDC_BF16;
+  a.b_bf16 = b_dtype == VDC_BF16;
+  a.S = (int32_t)S;
+  a.C = (int32_t)C;
+  a.nvec = (int32_t)(C / kVec);
+  a.rows = plan.rows;
+  a.bands = plan.bands;
+  g_launches.fetch_add(1, std::memory_order_relaxed);
+  return launch_fwd(plan, a, bias != nullptr, stream) == hipSuccess ? VDC_OK : VDC_EHIP;
+}
+
+extern "C" int conv1d_bwd(const void* x, const void* weight, int w_dtype, const void* bias,
+                          int b_dtype, const int32_t* cu_seqlens, int64_t num_docs,
+                          const void* dy, int64_t S, int64_t C, int policy, void* dx,
+                          void* dweight, int dw_dtype, void* dbias, int db_dtype,
+                          void* workspace, size_t ws_bytes, hipStream_t stream) {
+  int rc = check_sizes(S, C, num_docs);
+  if (rc) return rc;
+  if (!valid_dtype(w_dtype) || !valid_dtype(dw_dtype)) return VDC_EDTYPE;
+  if (bias && !valid_dtype(b_dtype)) return VDC_EDTYPE;
+  if (dbias && !valid_dtype(db_dtype)) return VDC_EDTYPE;
+  if (policy != VDC_SILU_GRAD_BF16 && policy != VDC_SILU_GRAD_FP32) return VDC_EDTYPE;
+  if (dbias && !bias) return VDC_ENOBIAS;
+  if (!dweight) return VDC_EINVAL;
+  if (!aligned(dweight, dtype_bytes(dw_dtype)) || (dbias && !aligned(dbias, dtype_bytes(db_dtype))))
+    return VDC_EALIGN;
+  const size_t dw_n = (size_t)C * 4 * dtype_bytes(dw_dtype);
+  const size_t db_n = dbias ? (size_t)C * dtype_bytes(db_dtype) : 0;
+  if (overlaps(dweight, dw_n, dbias, db_n)) return VDC_EINVAL;
+
+  if (S == 0) {
+    // No token: dx is empty and both gradients are zero.  No main or
+    // reduce kernel runs; under graph capture the zeros come from the
+    // reduce kernel run over zero partial rows instead of a memset node.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return VDC_EHIP;
+    if (cap == hipStreamCaptureStatusNone) {
+      if (hipMemsetAsync(dweight, 0, dw_n, stream) != hipSuccess) return VDC_EHIP;
+      if (dbias && hipMemsetAsync(dbias, 0, db_n, stream) != hipSuccess) return VDC_EHIP;
+      return VDC_OK;
+    }
+    Plan plan{};
+    plan.red_blocks = (int32_t)ceil_div(5 * C, kRedOut);
+    ReduceArgs r{};
+    r.part = nullptr;
+    r.dw = dweight;
+    r.db = dbias;
+    r.P = 0;
+    r.C = (int32_t)C;
+    r.rows_per_chunk = 0;
+    r.dw_bf16 = dw_dtype == VDC_BF16;
+    r.db_bf16 = db_dtype == VDC_BF16;
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    return launch_bwd_reduce(plan, r, false, stream) == hipSuccess ? VDC_OK : VDC_EHIP;
+  }
+
+  if (!x || !weight || !cu_seqlens || !dy || !dx) return VDC_EINVAL;
+  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || !aligned(weight, 16) ||
+      (bias && !aligned(bias, 16)))
+    return VDC_EALIGN;
+  const size_t need = workspace_bytes(VDC_BWD, S, C);
+  if (!workspace || ws_bytes < need) return VDC_EWORKSPACE;
+  if (!aligned(workspace, 16)) return VDC_EALIGN;
+
+  const size_t act = (size_t)S * (size_t)C * 2;
+  const size_t w_n = (size_t)C * 4 * dtype_bytes(w_dtype);
+  const size_t b_n = bias ? (size_t)C * dtype_bytes(b_dtype) : 0;
+  const size_t cu_n = (size_t)(num_docs + 1) * 4;
+  const void* ins[5] = {x, dy, weight, bias, cu_seqlens};
+  const size_t in_n[5] = {act, act, w_n, b_n, cu_n};
+  void* outs[4] = {dx, dweight, dbias, workspace};
+  const size_t out_n[4] = {act, dw_n, db_n, need};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 5; ++i)
+      if (overlaps(outs[o], out_n[o], ins[i], in_n[i])) return VDC_EINVAL;
+    for (int q = o + 1; q < 4; ++q)
+      if (overlaps(outs[o], out_n[o], outs[q], out_n[q])) return VDC_EINVAL;
+  }
+
+  const bool fp32_policy = policy == VDC_SILU_GRAD_FP32;
+  const Plan plan = make_plan(VDC_BWD, S, C, policy);
+  BwdArgs a{};
+  a.x = static_cast<const uint16_t*>(x);
+  a.dy = static_cast<const uint16_t*>(dy);
+  a.dx = static_cast<uint16_t*>(dx);
+  a.w = weight;
+  a.b = bias;
+  a.cu = cu_seqlens;
+  a.part = workspace;
+  a.num_docs = (int32_t)num_docs;
+  a.w_bf16 = w_dtype == VDC_BF16;
+  a.b_bf16 = b_dtype == VDC_BF16;
+  a.S = (int32_t)S;
+  a.C = (int32_t)C;
+  a.nvec = (int32_t)(C / kVec);
+  a.rows = plan.rows;
+  a.bands = plan.bands;
+  g_launches.fetch_add(1, std::memory_order_relaxed);
+  if (launch_bwd_main(plan, a, bias != nullptr, fp32_policy, stream) != hipSuccess) return VDC_EHIP;
+
+  ReduceArgs r{};
+  r.part = workspace;
+  r.dw = dweight;
+  r.db = dbias;
+  r.P = plan.bands;
+  r.C = (int32_t)C;
+  r.rows_per_chunk = plan.red_rows;
+  r.dw_bf16 = dw_dtype == VDC_BF16;
+  r.db_bf16 = db_dtype == VDC_BF16;
+  g_launches.fetch_add(1, std::memory_order_relaxed);
+  return launch_bwd_reduce(plan, r, fp32_policy, stream) == hipSuccess ? VDC_OK : VDC_EHIP;
+}
+
+extern "C" const char* conv1d_status_string(int status) {
+  switch (status) {
+    case VDC_OK: return "ok";
+    case VDC_EINVAL: return "invalid argument (size, missing pointer or overlapping buffers)";
+    case VDC_EDTYPE: return "unknown dtype or SiLU-derivative policy";
+    case VDC_EALIGN: return "misaligned tensor pointer";
+    case VDC_EWORKSPACE: return "workspace missing or too small";
+    case VDC_ENOBIAS: return "dbias requested without a bias";
+    case VDC_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" uint64_t conv1d_launch_count(void) {
+  return g_launches.load(std::memory_order_relaxed);
+}

@@ -1,0 +1,86 @@
+// Internal interface between the host entry points (vdc_api.cpp) and the
+// HIP kernels (vdc_kernels.hip).  Not installed; include/vdc.h is the ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace vdc {
+
+// Channels one lane owns: one 16-byte vector of eight BF16 values.
+constexpr int kVec = 8;
+// Threads per workgroup of the main kernels (four wave64).
+constexpr int kBlock = 256;
+// Rows one lane loads ahead and processes as one unrolled group.
+constexpr int kFwdGroup = 8;
+constexpr int kBwdGroup = 4;
+// Reduce kernel: outputs per workgroup and row chunks (one wave each).
+constexpr int kRedOut = 64;
+constexpr int kRedChunks = 8;
+
+// Everything a launch needs, decided on the host from (direction, S, C,
+// policy) alone - never from tensor contents.
+struct Plan {
+  int32_t rows;        // tokens per band (T)
+  int32_t bands;       // ceil(S / T); also the backward's partial rows
+  int64_t lanes;       // bands * C / 8
+  int32_t blocks;      // main-kernel workgroups
+  int32_t acc_bytes;   // backward partial element: 4 (FP32) or 8 (FP64)
+  int32_t red_blocks;  // reduce workgroups
+  int32_t red_rows;    // partial rows per reduce chunk
+};
+
+struct FwdArgs {
+  const uint16_t* x;
+  uint16_t* y;
+  const void* w;
+  const void* b;
+  const int32_t* cu;
+  int32_t num_docs;
+  int32_t w_bf16;
+  int32_t b_bf16;
+  int32_t S;
+  int32_t C;
+  int32_t nvec;        // C / 8
+  int32_t rows;        // T
+  int32_t bands;
+};
+
+struct BwdArgs {
+  const uint16_t* x;
+  const uint16_t* dy;
+  uint16_t* dx;
+  const void* w;
+  const void* b;
+  const int32_t* cu;
+  void* part;          // [bands][5][C] of FP32 or FP64
+  int32_t num_docs;
+  int32_t w_bf16;
+  int32_t b_bf16;
+  int32_t S;
+  int32_t C;
+  int32_t nvec;
+  int32_t rows;
+  int32_t bands;
+};
+
+struct ReduceArgs {
+  const void* part;    // [P][5][C]
+  void* dw;            // [C][4]
+  void* db;            // [C] or null
+  int32_t P;
+  int32_t C;
+  int32_t rows_per_chunk;
+  int32_t dw_bf16;
+  int32_t db_bf16;
+};
+
+// Launchers (return the hipError_t of the launch).
+hipError_t launch_fwd(const Plan& plan, const FwdArgs& a, bool has_bias, hipStream_t s);
+hipError_t launch_bwd_main(const Plan& plan, const BwdArgs& a, bool has_bias, bool fp32_policy,
+                           hipStream_t s);
+hipError_t launch_bwd_reduce(const Plan& plan, const ReduceArgs& a, bool fp64, hipStream_t s);
+
+}  // namespace vdc
