@@ -35,9 +35,9 @@
  *  - Pointers to tensors are DEVICE pointers; sizes are element counts.
  *    Tensors are dense and row-major; x / dy / y / dx are [S][C] bf16 and
  *    must be 16-byte aligned; weight is [C][4] and bias [C], both 16-byte
- *    aligned; dweight [C][4] and
- *    dbias [C] are 4-byte (FP32) or 2-byte (BF16) aligned; each is FP32 or
- *    BF16 as its dtype argument says; cu_seqlens is int32 [num_docs + 1].
+ *    aligned; dweight [C][4] and dbias [C] are 4-byte (FP32) or 2-byte
+ *    (BF16) aligned; each is FP32 or BF16 as its dtype argument says;
+ *    cu_seqlens is int32 [num_docs + 1].
  *  - The caller owns every buffer.  The library allocates nothing, frees
  *    nothing, keeps no per-call state, never synchronizes, and never reads
  *    device memory on the host (in particular not cu_seqlens, whose
@@ -170,12 +170,13 @@ const char *conv1d_status_string(int status);
 /*
  * conv1d_plan - the launch plan a call with these sizes would use
  * (introspection for tests and benchmarks; enqueues nothing).
- * Fills out[0..7] = { rows per band, bands (= partial rows of the
- * backward), lanes (bands * C/8), main-kernel workgroups, threads per
- * workgroup, partial element bytes (0 forward, 4 or 8 backward),
- * reduce-kernel workgroups, reduce chunks }.  Returns a vdc_status.
+ * Fills out[0..9] = { rows per band, bands (= partial rows of the
+ * backward), lanes (bands * C / channels per lane), main-kernel workgroups,
+ * threads per workgroup, partial element bytes (0 forward, 4 or 8
+ * backward), reduce-kernel workgroups, reduce chunks, channels per lane,
+ * 0 }.  Returns a vdc_status.
  */
-int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int64_t out[8]);
+int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int64_t out[10]);
 
 /* conv1d_launch_count - kernels this process has launched through the
  * library so far (a diagnostic counter, e.g. to check that S == 0

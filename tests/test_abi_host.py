@@ -138,7 +138,7 @@ def test_workspace_bytes(lib):
     assert lib.workspace_bytes(7, 100, 64) == 0
     for S, C in ((1000, 64), (65536, 4096), (262144, 520), (131072, 8192), (1, 8)):
         n = lib.workspace_bytes(BWD, S, C)
-        out = (ctypes.c_int64 * 8)()
+        out = (ctypes.c_int64 * 10)()
         assert lib.conv1d_plan(BWD, S, C, 1, out) == OK
         rows, bands = out[0], out[1]
         assert bands == -(-S // rows)
@@ -150,15 +150,16 @@ def test_workspace_bytes(lib):
 def test_plans_depend_on_shape_only(lib):
     for d in (FWD, BWD):
         for S, C in ((65536, 4096), (262144, 520), (1000, 64)):
-            a, b = (ctypes.c_int64 * 8)(), (ctypes.c_int64 * 8)()
+            a, b = (ctypes.c_int64 * 10)(), (ctypes.c_int64 * 10)()
             assert lib.conv1d_plan(d, S, C, 0, a) == OK
             assert lib.conv1d_plan(d, S, C, 0, b) == OK
             assert list(a) == list(b)
-            rows, bands, lanes, blocks, threads = a[0], a[1], a[2], a[3], a[4]
+            rows, bands, lanes, blocks, threads, vec = a[0], a[1], a[2], a[3], a[4], a[8]
+            assert vec in (4, 8) and C % vec == 0
             assert rows % 8 == 0 and rows >= 16
-            assert lanes == bands * (C // 8) and blocks * threads >= lanes
+            assert lanes == bands * (C // vec) and blocks * threads >= lanes
             # a wave's span of rows stays far inside 32-bit byte offsets
-            span = (-(-64 // (C // 8)) + 1) * rows + 8
+            span = (-(-64 // (C // vec)) + 1) * rows + 8
             assert span * C * 2 < 2 ** 31
 
 

@@ -20,8 +20,10 @@ std::atomic<uint64_t> g_launches{0};
 constexpr int64_t kMaxC = int64_t(1) << 20;
 constexpr int64_t kMaxS = (int64_t(1) << 31) - 1;
 // Lanes that keep the whole chip busy at the occupancy these kernels reach
-// (256 CUs x 8 wave64).
-constexpr int64_t kFillLanes = 256 * 8 * 64;
+// (256 CUs x 16 wave64).
+constexpr int64_t kFillLanes = 256 * 16 * 64;
+// Smallest lane vector: the size checks below are made for it.
+constexpr int64_t kMinVec = 4;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -46,8 +48,10 @@ int64_t wave_span_rows(int64_t nvec, int64_t rows) {
 // problem is too small to fill the chip.  Backward: 256, more for large
 // problems (fewer partial rows) and fewer for small ones.  A function of
 // (direction, S, C) only.
+int32_t pick_vec(int dir) { return dir == VDC_FWD ? kFwdVec : kBwdVec; }
+
 int32_t pick_rows(int dir, int64_t S, int64_t C) {
-  const int64_t nvec = C / kVec;
+  const int64_t nvec = C / pick_vec(dir);
   int64_t rows = dir == VDC_FWD ? 64 : 256;
   const int64_t lo = 16;
   auto lanes = [&](int64_t r) { return ceil_div(S, r) * nvec; };
@@ -60,9 +64,10 @@ int32_t pick_rows(int dir, int64_t S, int64_t C) {
 
 Plan make_plan(int dir, int64_t S, int64_t C, int policy) {
   Plan p{};
+  p.vec = pick_vec(dir);
   p.rows = pick_rows(dir, S, C);
   p.bands = (int32_t)ceil_div(S, p.rows);
-  p.lanes = (int64_t)p.bands * (C / kVec);
+  p.lanes = (int64_t)p.bands * (C / p.vec);
   p.blocks = (int32_t)ceil_div(p.lanes, kBlock);
   p.acc_bytes = dir == VDC_FWD ? 0 : (policy == VDC_SILU_GRAD_FP32 ? 8 : 4);
   p.red_blocks = dir == VDC_FWD ? 0 : (int32_t)ceil_div(5 * C, kRedOut);
@@ -71,12 +76,12 @@ Plan make_plan(int dir, int64_t S, int64_t C, int policy) {
 }
 
 int check_sizes(int64_t S, int64_t C, int64_t num_docs) {
-  if (C <= 0 || C % kVec != 0 || C > kMaxC) return VDC_EINVAL;
+  if (C <= 0 || C % 8 != 0 || C > kMaxC) return VDC_EINVAL;
   if (S < 0 || S > kMaxS) return VDC_EINVAL;
   if (num_docs < 0 || num_docs > kMaxS - 1) return VDC_EINVAL;
   if (S > 0 && num_docs < 1) return VDC_EINVAL;
   // The planner must find a band size whose wave span fits 32-bit offsets.
-  if (wave_span_rows(C / kVec, 16) * C * 2 >= (int64_t(1) << 31)) return VDC_EINVAL;
+  if (wave_span_rows(C / kMinVec, 16) * C * 2 >= (int64_t(1) << 31)) return VDC_EINVAL;
   return VDC_OK;
 }
 
@@ -94,7 +99,7 @@ extern "C" size_t workspace_bytes(int direction, int64_t S, int64_t C) {
   return (size_t)p.bands * 5 * (size_t)C * 8;
 }
 
-extern "C" int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int64_t out[8]) {
+extern "C" int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int64_t out[10]) {
   if (!out) return VDC_EINVAL;
   if (direction != VDC_FWD && direction != VDC_BWD) return VDC_EINVAL;
   if (direction == VDC_BWD && policy != VDC_SILU_GRAD_BF16 && policy != VDC_SILU_GRAD_FP32)
@@ -110,6 +115,8 @@ extern "C" int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int6
   out[5] = p.acc_bytes;
   out[6] = p.red_blocks;
   out[7] = kRedChunks;
+  out[8] = p.vec;
+  out[9] = 0;
   return VDC_OK;
 }
 
@@ -145,7 +152,7 @@ extern "C" int conv1d_fwd(const void* x, const void* weight, int w_dtype, const 
   a.b_bf16 = b_dtype == VDC_BF16;
   a.S = (int32_t)S;
   a.C = (int32_t)C;
-  a.nvec = (int32_t)(C / kVec);
+  a.nvec = (int32_t)(C / plan.vec);
   a.rows = plan.rows;
   a.bands = plan.bands;
   g_launches.fetch_add(1, std::memory_order_relaxed);
@@ -235,7 +242,7 @@ extern "C" int conv1d_bwd(const void* x, const void* weight, int w_dtype, const 
   a.b_bf16 = b_dtype == VDC_BF16;
   a.S = (int32_t)S;
   a.C = (int32_t)C;
-  a.nvec = (int32_t)(C / kVec);
+  a.nvec = (int32_t)(C / plan.vec);
   a.rows = plan.rows;
   a.bands = plan.bands;
   g_launches.fetch_add(1, std::memory_order_relaxed);

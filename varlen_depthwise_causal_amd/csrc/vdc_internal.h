@@ -9,8 +9,15 @@
 
 namespace vdc {
 
-// Channels one lane owns: one 16-byte vector of eight BF16 values.
-constexpr int kVec = 8;
+// Channels one lane owns (a vector of 4 or 8 BF16 values), per direction.
+#ifndef VDC_FWD_VEC
+#define VDC_FWD_VEC 4
+#endif
+#ifndef VDC_BWD_VEC
+#define VDC_BWD_VEC 4
+#endif
+constexpr int kFwdVec = VDC_FWD_VEC;
+constexpr int kBwdVec = VDC_BWD_VEC;
 // Threads per workgroup of the main kernels (four wave64).
 constexpr int kBlock = 256;
 // Rows one lane loads ahead and processes as one unrolled group.
@@ -23,9 +30,10 @@ constexpr int kRedChunks = 8;
 // Everything a launch needs, decided on the host from (direction, S, C,
 // policy) alone - never from tensor contents.
 struct Plan {
+  int32_t vec;         // channels per lane (V)
   int32_t rows;        // tokens per band (T)
   int32_t bands;       // ceil(S / T); also the backward's partial rows
-  int64_t lanes;       // bands * C / 8
+  int64_t lanes;       // bands * C / V
   int32_t blocks;      // main-kernel workgroups
   int32_t acc_bytes;   // backward partial element: 4 (FP32) or 8 (FP64)
   int32_t red_blocks;  // reduce workgroups
@@ -43,7 +51,7 @@ struct FwdArgs {
   int32_t b_bf16;
   int32_t S;
   int32_t C;
-  int32_t nvec;        // C / 8
+  int32_t nvec;        // C / V
   int32_t rows;        // T
   int32_t bands;
 };

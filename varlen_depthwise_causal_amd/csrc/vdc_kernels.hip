@@ -5,18 +5,20 @@
 // flashinfer.cake_causal_conv1d_train (cake_causal_conv1d_train_forward:
 // Returns; cake_causal_conv1d_train_backward: Description, Returns).  It is
 // a 4-tap stencil along the token axis followed by an elementwise SiLU, so
-// it is bound by HBM traffic, not by matrix throughput: no MFMA here.
+// it is bound by HBM traffic and VALU issue, not by matrix throughput: no
+// MFMA here.
 //
 // Work decomposition (same for every kernel of the main path):
-//  * A lane owns one 16-byte vector of 8 consecutive BF16 channels and a
-//    band of T consecutive tokens, and walks the band row by row.  Lanes are
-//    numbered (band, vector) -> band * (C/8) + vector, so the 64 lanes of a
-//    wave read 64 consecutive vectors of a row (1 KiB, fully coalesced) and,
-//    when C/8 is not a multiple of 64, simply continue into the next band.
+//  * A lane owns V consecutive BF16 channels (one 8- or 16-byte vector) and
+//    a band of T consecutive tokens, and walks the band row by row.  Lanes
+//    are numbered (band, vector) -> band * (C/V) + vector, so the 64 lanes of
+//    a wave read 64 consecutive vectors of a row (fully coalesced) and, when
+//    C/V is not a multiple of 64, simply continue into the next band.
 //  * A lane keeps the previous three rows of x in registers; at a document
 //    start the window is cleared, which is exactly the zero history the
 //    forward prescribes, so no tap needs a mask.  The document starts are
-//    found by one binary search of cu_seqlens per lane and a forward walk.
+//    found by one binary search of cu_seqlens per lane and a forward walk;
+//    groups of rows with no start nearby take a branch without any check.
 //  * Tensors are addressed through buffer resources based at the wave's
 //    first row, with 32-bit per-lane offsets: rows past S read as zero and
 //    their stores are dropped by the hardware range check.
@@ -35,6 +37,7 @@ namespace vdc {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -46,32 +49,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kDeep = -80.0f;
 // Word 3 of a raw (untyped, unswizzled) gfx9 buffer resource.
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache-policy bits of the streaming accesses: "nt" (non-temporal).  Every
+// activation byte is touched once per call, so none is worth keeping.
+constexpr int kStream = 2;
 
 // ---------------------------------------------------------------- BF16 --
 
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
-__device__ __forceinline__ void unpack8(u32x4 v, float (&f)[8]) {
-  f[0] = bf_lo(v.x); f[1] = bf_hi(v.x);
-  f[2] = bf_lo(v.y); f[3] = bf_hi(v.y);
-  f[4] = bf_lo(v.z); f[5] = bf_hi(v.z);
-  f[6] = bf_lo(v.w); f[7] = bf_hi(v.w);
-}
-
 // Two FP32 -> packed BF16 pair, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   bf16x2 h = __builtin_convertvector((f32x2){a, b}, bf16x2);
   return __builtin_bit_cast(uint32_t, h);
-}
-
-__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
-  u32x4 r;
-  r.x = pack2(f[0], f[1]);
-  r.y = pack2(f[2], f[3]);
-  r.z = pack2(f[4], f[5]);
-  r.w = pack2(f[6], f[7]);
-  return r;
 }
 
 // FP32 -> BF16 bits, round to nearest even, by integer arithmetic; exact for
@@ -95,17 +85,50 @@ __device__ __forceinline__ uint16_t bf16_bits_from_f64(double d) {
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// ------------------------------------------------------ buffer access --
+// ------------------------------------------------ lane vectors (V = 4, 8) --
+
+template <int V> struct Vec;
+template <> struct Vec<8> {
+  typedef u32x4 raw;
+  __device__ static __forceinline__ raw load(rsrc_t r, int32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream);
+  }
+  __device__ static __forceinline__ void store(rsrc_t r, int32_t off, raw v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStream);
+  }
+  __device__ static __forceinline__ raw zero() { return (raw){0u, 0u, 0u, 0u}; }
+};
+template <> struct Vec<4> {
+  typedef u32x2 raw;
+  __device__ static __forceinline__ raw load(rsrc_t r, int32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kStream);
+  }
+  __device__ static __forceinline__ void store(rsrc_t r, int32_t off, raw v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStream);
+  }
+  __device__ static __forceinline__ raw zero() { return (raw){0u, 0u}; }
+};
+
+template <int V>
+__device__ __forceinline__ void unpack(typename Vec<V>::raw v, float (&f)[V]) {
+#pragma unroll
+  for (int d = 0; d < V / 2; ++d) {
+    f[2 * d] = bf_lo(v[d]);
+    f[2 * d + 1] = bf_hi(v[d]);
+  }
+}
+
+template <int V>
+__device__ __forceinline__ typename Vec<V>::raw pack(const float (&f)[V]) {
+  typename Vec<V>::raw r;
+#pragma unroll
+  for (int d = 0; d < V / 2; ++d) r[d] = pack2(f[2 * d], f[2 * d + 1]);
+  return r;
+}
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            kRsrcWord3);
-}
-__device__ __forceinline__ u32x4 ld16(rsrc_t r, int32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-__device__ __forceinline__ void st16(rsrc_t r, int32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
 }
 
 // Bytes from row `row` to the end of an [S][C] BF16 tensor, clamped to what
@@ -118,14 +141,15 @@ __device__ __forceinline__ uint32_t span_bytes(int32_t S, int32_t C, int32_t row
 
 // ------------------------------------------------------- parameters --
 
-// weight [C][4] (FP32: one 16-byte vector per channel; BF16: two channels
-// per 16-byte vector) -> w[k][i] for the lane's channels c0 .. c0+7.
+// weight [C][4] -> w[k][i] for the lane's channels c0 .. c0+V-1
+// (FP32: one 16-byte vector per channel; BF16: one 8-byte vector).
+template <int V>
 __device__ __forceinline__ void load_weights(const void* w, int bf16, uint32_t c0,
-                                             float (&wk)[4][8]) {
+                                             float (&wk)[4][V]) {
   if (!bf16) {
     const u32x4* p = reinterpret_cast<const u32x4*>(w) + c0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < V; ++i) {
       u32x4 v = p[i];
       wk[0][i] = __uint_as_float(v.x);
       wk[1][i] = __uint_as_float(v.y);
@@ -133,32 +157,40 @@ __device__ __forceinline__ void load_weights(const void* w, int bf16, uint32_t c
       wk[3][i] = __uint_as_float(v.w);
     }
   } else {
-    const u32x4* p = reinterpret_cast<const u32x4*>(w) + c0 / 2;
+    const u32x2* p = reinterpret_cast<const u32x2*>(w) + c0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      u32x4 v = p[q];
-      wk[0][2 * q] = bf_lo(v.x);
-      wk[1][2 * q] = bf_hi(v.x);
-      wk[2][2 * q] = bf_lo(v.y);
-      wk[3][2 * q] = bf_hi(v.y);
-      wk[0][2 * q + 1] = bf_lo(v.z);
-      wk[1][2 * q + 1] = bf_hi(v.z);
-      wk[2][2 * q + 1] = bf_lo(v.w);
-      wk[3][2 * q + 1] = bf_hi(v.w);
+    for (int i = 0; i < V; ++i) {
+      u32x2 v = p[i];
+      wk[0][i] = bf_lo(v.x);
+      wk[1][i] = bf_hi(v.x);
+      wk[2][i] = bf_lo(v.y);
+      wk[3][i] = bf_hi(v.y);
     }
   }
 }
 
-__device__ __forceinline__ void load_bias(const void* b, int bf16, uint32_t c0, float (&bv)[8]) {
+template <int V>
+__device__ __forceinline__ void load_bias(const void* b, int bf16, uint32_t c0, float (&bv)[V]) {
   if (!bf16) {
     const u32x4* p = reinterpret_cast<const u32x4*>(b) + c0 / 4;
-    u32x4 v0 = p[0], v1 = p[1];
-    bv[0] = __uint_as_float(v0.x); bv[1] = __uint_as_float(v0.y);
-    bv[2] = __uint_as_float(v0.z); bv[3] = __uint_as_float(v0.w);
-    bv[4] = __uint_as_float(v1.x); bv[5] = __uint_as_float(v1.y);
-    bv[6] = __uint_as_float(v1.z); bv[7] = __uint_as_float(v1.w);
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) {
+      u32x4 v = p[q];
+      bv[4 * q + 0] = __uint_as_float(v.x);
+      bv[4 * q + 1] = __uint_as_float(v.y);
+      bv[4 * q + 2] = __uint_as_float(v.z);
+      bv[4 * q + 3] = __uint_as_float(v.w);
+    }
   } else {
-    unpack8(reinterpret_cast<const u32x4*>(b)[c0 / 8], bv);
+    const u32x2* p = reinterpret_cast<const u32x2*>(b) + c0 / 4;
+#pragma unroll
+    for (int q = 0; q < V / 4; ++q) {
+      u32x2 v = p[q];
+      bv[4 * q + 0] = bf_lo(v.x);
+      bv[4 * q + 1] = bf_hi(v.x);
+      bv[4 * q + 2] = bf_lo(v.y);
+      bv[4 * q + 3] = bf_hi(v.y);
+    }
   }
 }
 
@@ -218,10 +250,87 @@ __device__ __forceinline__ float silu_grad_deep(float z) {
   return (sigmoid_scaled64(z) * (1.0f + z)) * 0x1p-64f;
 }
 
-// The preactivation, in the one fixed order used by both directions:
+// ---------------------------------- SiLU' of every BF16 value (table) --
+//
+// Under the "bf16" policy SiLU' is only ever evaluated at BF16 values, so it
+// is read from a table of its binary32 roundings, computed here at compile
+// time in double precision.  The table covers the BF16 magnitudes with
+// biased exponents kLutExpLo .. kLutExpHi (2^-25 <= |z| < 256), both signs.
+// Smaller magnitudes clamp to the smallest entry (SiLU' rounds to 1/2
+// there), larger ones to the largest (SiLU' rounds to 1 for z > 0 and to
+// 0 for z < 0).
+
+constexpr int kLutExpLo = 102;
+constexpr int kLutExpHi = 134;
+constexpr uint32_t kLutLo = uint32_t(kLutExpLo) << 7;
+constexpr uint32_t kLutHi = (uint32_t(kLutExpHi + 1) << 7) - 1;
+constexpr int kLutN = int(kLutHi - kLutLo + 1);  // entries per sign
+
+constexpr double cx_pow2(int e) {
+  double r = 1.0, b = e >= 0 ? 2.0 : 0.5;
+  int n = e >= 0 ? e : -e;
+  while (n) {
+    if (n & 1) r *= b;
+    b *= b;
+    n >>= 1;
+  }
+  return r;
+}
+
+// exp(x) for |x| < 700: x = k ln 2 + r with |r| <= ln 2 / 2, then a Taylor
+// series for exp(r) (terms beyond r^27/27! are below 2^-100) times 2^k.
+constexpr double cx_exp(double x) {
+  constexpr double kLn2 = 0.6931471805599453;
+  double kd = x / kLn2;
+  long long k = (long long)(kd >= 0 ? kd + 0.5 : kd - 0.5);
+  double r = x - double(k) * kLn2;
+  double term = 1.0, sum = 1.0;
+  for (int n = 1; n <= 27; ++n) {
+    term = term * r / double(n);
+    sum += term;
+  }
+  return sum * cx_pow2(int(k));
+}
+
+constexpr float cx_silu_grad(double z) {
+  double e = cx_exp(-z);
+  double s = 1.0 / (1.0 + e);
+  double one_minus_s = e / (1.0 + e);
+  return float(s * (1.0 + z * one_minus_s));
+}
+
+struct SiluGradTable {
+  float v[2 * kLutN];  // [0, N): +z, [N, 2N): -z, index = magnitude pattern - kLutLo
+};
+
+constexpr SiluGradTable make_silu_grad_table() {
+  SiluGradTable t{};
+  for (int i = 0; i < kLutN; ++i) {
+    const uint32_t a = kLutLo + uint32_t(i);
+    const int e = int(a >> 7);
+    const double m = 1.0 + double(a & 127u) / 128.0;
+    const double z = m * cx_pow2(e - 127);
+    t.v[i] = cx_silu_grad(z);
+    t.v[kLutN + i] = cx_silu_grad(-z);
+  }
+  return t;
+}
+
+__constant__ SiluGradTable kSiluGradTable = make_silu_grad_table();
+
+// Table index of BF16 bit pattern `bits` (16 bits, sign included).
+__device__ __forceinline__ uint32_t lut_index(uint32_t bits) {
+  uint32_t a = bits & 0x7fffu;
+  a = min(max(a, kLutLo), kLutHi);
+  return (a - kLutLo) + ((bits >> 15) & 1u) * uint32_t(kLutN);
+}
+
+// ------------------------------------------------- the preactivation --
+
+// One fixed order used by both directions:
 // ((w0 x[t-3] + w1 x[t-2]) + w2 x[t-1]) + w3 x[t], then + bias.
-template <bool kBias>
-__device__ __forceinline__ float preact(const float (&w)[4][8], const float (&bv)[8], int i,
+template <bool kBias, int V>
+__device__ __forceinline__ float preact(const float (&w)[4][V], const float (&bv)[V], int i,
                                         float xm3, float xm2, float xm1, float x0) {
   float p = w[0][i] * xm3;
   p = __builtin_fmaf(w[1][i], xm2, p);
@@ -239,6 +348,7 @@ struct Lane {
   int32_t off;       // byte offset of (t0 - 3, vec) from the base
 };
 
+template <int V>
 __device__ __forceinline__ bool lane_coords(int32_t nvec, int32_t rows, int32_t bands, int32_t C,
                                             Lane& L) {
   const uint32_t g = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
@@ -248,24 +358,58 @@ __device__ __forceinline__ bool lane_coords(int32_t nvec, int32_t rows, int32_t 
   L.t0 = (int32_t)L.band * rows;
   const int32_t first_band = __builtin_amdgcn_readfirstlane((int32_t)L.band);
   L.base_row = max(first_band * rows - 3, 0);
-  L.off = (L.t0 - 3 - L.base_row) * (C * 2) + (int32_t)L.vec * 16;
+  L.off = (L.t0 - 3 - L.base_row) * (C * 2) + (int32_t)L.vec * (V * 2);
   return true;
 }
 
 // ===================================================== forward kernel ==
 
-template <bool kBias>
+template <bool kBias, int V>
+__device__ __forceinline__ typename Vec<V>::raw fwd_row(const float (&w)[4][V],
+                                                        const float (&bv)[V],
+                                                        const float (&h3)[V], const float (&h2)[V],
+                                                        const float (&h1)[V],
+                                                        const float (&xc)[V]) {
+  float p[V], yv[V];
+  float pmin = 0.0f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    p[i] = preact<kBias, V>(w, bv, i, h3[i], h2[i], h1[i], xc[i]);
+    pmin = __builtin_fminf(pmin, p[i]);
+    yv[i] = p[i] * sigmoid_fast(p[i]);
+  }
+  typename Vec<V>::raw out = pack<V>(yv);
+  if (pmin < kDeep) {
+    // Rare: some p is so negative that sigmoid(p) underflows on the fast
+    // path; redo those values in scaled form and round them exactly.
+#pragma unroll
+    for (int d = 0; d < V / 2; ++d) {
+      uint32_t h[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int i = 2 * d + q;
+        const float yd = (p[i] * sigmoid_scaled64(p[i])) * 0x1p-64f;
+        h[q] = p[i] < kDeep ? bf16_bits_rne(yd) : bf16_bits_rne(yv[i]);
+      }
+      out[d] = h[0] | (h[1] << 16);
+    }
+  }
+  return out;
+}
+
+template <bool kBias, int V>
 __global__ __launch_bounds__(kBlock) void fwd_kernel(FwdArgs a) {
+  typedef Vec<V> VT;
   Lane L;
-  if (!lane_coords(a.nvec, a.rows, a.bands, a.C, L)) return;
+  if (!lane_coords<V>(a.nvec, a.rows, a.bands, a.C, L)) return;
   const int32_t row_bytes = a.C * 2;
   const uint32_t nrec = span_bytes(a.S, a.C, L.base_row);
   const rsrc_t rx = make_rsrc(a.x + (int64_t)L.base_row * a.C, nrec);
   const rsrc_t ry = make_rsrc(a.y + (int64_t)L.base_row * a.C, nrec);
 
-  float w[4][8], bv[8];
-  load_weights(a.w, a.w_bf16, L.vec * kVec, w);
-  if (kBias) load_bias(a.b, a.b_bf16, L.vec * kVec, bv);
+  float w[4][V], bv[V];
+  load_weights<V>(a.w, a.w_bf16, L.vec * V, w);
+  if (kBias) load_bias<V>(a.b, a.b_bf16, L.vec * V, bv);
 
   int32_t r = L.t0 - 3;
   int32_t off = L.off;
@@ -273,64 +417,53 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(FwdArgs a) {
   walk.init(a.cu, a.num_docs, max(r, 0));
 
   // Window of the three previous rows: h1 = x[r-1], h2 = x[r-2], h3 = x[r-3].
-  float h1[8], h2[8], h3[8];
+  float h1[V], h2[V], h3[V];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) h1[i] = h2[i] = h3[i] = 0.0f;
+  for (int i = 0; i < V; ++i) h1[i] = h2[i] = h3[i] = 0.0f;
 
   // Halo rows t0-3 .. t0-1 (before the first token nothing is read).
 #pragma unroll
   for (int q = 0; q < 3; ++q, ++r, off += row_bytes) {
-    u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-    if (r >= 0) v = ld16(rx, off);
+    typename VT::raw v = VT::zero();
+    if (r >= 0) v = VT::load(rx, off);
     if (r == walk.next) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h1[i] = h2[i] = 0.0f;
+      for (int i = 0; i < V; ++i) h1[i] = h2[i] = 0.0f;
       walk.advance(r);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h3[i] = h2[i], h2[i] = h1[i];
-    unpack8(v, h1);
+    for (int i = 0; i < V; ++i) h3[i] = h2[i], h2[i] = h1[i];
+    unpack<V>(v, h1);
   }
 
   for (int32_t done = 0; done < a.rows; done += kFwdGroup) {
-    u32x4 raw[kFwdGroup];
+    typename VT::raw raw[kFwdGroup];
 #pragma unroll
-    for (int g = 0; g < kFwdGroup; ++g) raw[g] = ld16(rx, off + g * row_bytes);
-    const bool quiet = walk.next > r + (kFwdGroup - 1);
+    for (int g = 0; g < kFwdGroup; ++g) raw[g] = VT::load(rx, off + g * row_bytes);
+    if (walk.next > r + (kFwdGroup - 1)) {
+      // No document starts in this group.
 #pragma unroll
-    for (int g = 0; g < kFwdGroup; ++g) {
-      if (!quiet && r + g == walk.next) {
+      for (int g = 0; g < kFwdGroup; ++g) {
+        float xc[V];
+        unpack<V>(raw[g], xc);
+        VT::store(ry, off + g * row_bytes, fwd_row<kBias, V>(w, bv, h3, h2, h1, xc));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) h1[i] = h2[i] = h3[i] = 0.0f;
-        walk.advance(r + g);
+        for (int i = 0; i < V; ++i) h3[i] = h2[i], h2[i] = h1[i], h1[i] = xc[i];
       }
-      float xc[8], p[8], yv[8];
-      unpack8(raw[g], xc);
-      float pmin = 0.0f;
+    } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = preact<kBias>(w, bv, i, h3[i], h2[i], h1[i], xc[i]);
-        pmin = __builtin_fminf(pmin, p[i]);
-        yv[i] = p[i] * sigmoid_fast(p[i]);
-      }
-      u32x4 out = pack8(yv);
-      if (pmin < kDeep) {
-        // Rare: some p is so negative that sigmoid(p) underflows on the fast
-        // path; redo those values in scaled form and round them exactly.
-        uint32_t hbits[8];
+      for (int g = 0; g < kFwdGroup; ++g) {
+        if (r + g == walk.next) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          float yd = (p[i] * sigmoid_scaled64(p[i])) * 0x1p-64f;
-          hbits[i] = p[i] < kDeep ? bf16_bits_rne(yd) : bf16_bits_rne(yv[i]);
+          for (int i = 0; i < V; ++i) h1[i] = h2[i] = h3[i] = 0.0f;
+          walk.advance(r + g);
         }
-        out.x = hbits[0] | (hbits[1] << 16);
-        out.y = hbits[2] | (hbits[3] << 16);
-        out.z = hbits[4] | (hbits[5] << 16);
-        out.w = hbits[6] | (hbits[7] << 16);
-      }
-      st16(ry, off + g * row_bytes, out);
+        float xc[V];
+        unpack<V>(raw[g], xc);
+        VT::store(ry, off + g * row_bytes, fwd_row<kBias, V>(w, bv, h3, h2, h1, xc));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h3[i] = h2[i], h2[i] = h1[i], h1[i] = xc[i];
+        for (int i = 0; i < V; ++i) h3[i] = h2[i], h2[i] = h1[i], h1[i] = xc[i];
+      }
     }
     r += kFwdGroup;
     off += kFwdGroup * row_bytes;
@@ -339,87 +472,107 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(FwdArgs a) {
 
 // ================================================ backward main kernel ==
 
-template <typename Acc>
+__device__ __forceinline__ float fma_acc(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+__device__ __forceinline__ double fma_acc(double a, double b, double c) { return __builtin_fma(a, b, c); }
+
+template <typename Acc, int V>
 struct Partials {
-  Acc v[5][8];  // taps k = 0..3, then the bias term
+  Acc v[5][V];  // taps k = 0..3, then the bias term
 };
 
-// One row of the backward: recompute p, form dpre, accumulate partials and
-// emit dx of the row three tokens back.
-//  hist: bit 0 = row v is a document start, bit 1 = row v-1, bit 2 = row v-2.
-template <bool kBias, bool kBf16Policy, typename Acc>
-__device__ __forceinline__ void bwd_row(const float (&w)[4][8], const float (&bv)[8],
-                                        const float (&xc)[8], u32x4 dyraw,
-                                        float (&h1)[8], float (&h2)[8], float (&h3)[8],
-                                        float (&d1)[8], float (&d2)[8], float (&d3)[8],
-                                        Partials<Acc>& acc, bool accumulate, bool emit,
-                                        uint32_t hist, bool masked, rsrc_t rdx, int32_t dx_off) {
-  float dyv[8], p[8], dp[8];
-  unpack8(dyraw, dyv);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = preact<kBias>(w, bv, i, h3[i], h2[i], h1[i], xc[i]);
-  float z[8];
+// dpre = dy * SiLU'(z) for the lane's V channels of one row.
+template <bool kBf16Policy, int V>
+__device__ __forceinline__ void dpre_row(const float (&p)[V], const float (&dyv)[V],
+                                         const float* lut, float (&dp)[V]) {
   if (kBf16Policy) {
+    // z = bf16(p); SiLU'(z) from the table.
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      uint32_t h = pack2(p[i], p[i + 1]);
-      z[i] = bf_lo(h);
-      z[i + 1] = bf_hi(h);
+    for (int d = 0; d < V / 2; ++d) {
+      const uint32_t h = pack2(p[2 * d], p[2 * d + 1]);
+      dp[2 * d] = dyv[2 * d] * lut[lut_index(h & 0xffffu)];
+      dp[2 * d + 1] = dyv[2 * d + 1] * lut[lut_index(h >> 16)];
     }
   } else {
+    float zmin = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) z[i] = p[i];
-  }
-  float zmin = 0.0f;
+    for (int i = 0; i < V; ++i) {
+      zmin = __builtin_fminf(zmin, p[i]);
+      dp[i] = dyv[i] * silu_grad_fast(p[i]);
+    }
+    if (zmin < kDeep) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    zmin = __builtin_fminf(zmin, z[i]);
-    dp[i] = dyv[i] * silu_grad_fast(z[i]);
+      for (int i = 0; i < V; ++i)
+        if (p[i] < kDeep) dp[i] = dyv[i] * silu_grad_deep(p[i]);
+    }
   }
-  if (zmin < kDeep) {
+}
+
+// One row v of the backward: recompute p, form dpre, accumulate partials
+// (rows of the band) and emit dx of row v-3 (from the band's fourth row on).
+// kMasked: a document starts within rows v-2 .. v (bits of `hist`: bit 0 =
+// row v, bit 1 = row v-1, bit 2 = row v-2); then later rows count toward
+// dx[v-3] only if no start lies between.
+template <bool kBias, bool kBf16Policy, bool kMasked, typename Acc, int V>
+__device__ __forceinline__ void bwd_row(const float (&w)[4][V], const float (&bv)[V],
+                                        const float* lut, const float (&xc)[V],
+                                        typename Vec<V>::raw dyraw, float (&h1)[V],
+                                        float (&h2)[V], float (&h3)[V], float (&d1)[V],
+                                        float (&d2)[V], float (&d3)[V], Partials<Acc, V>& acc,
+                                        bool accumulate, bool emit, uint32_t hist, rsrc_t rdx,
+                                        int32_t dx_off) {
+  float dyv[V], p[V], dp[V];
+  unpack<V>(dyraw, dyv);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (z[i] < kDeep) dp[i] = dyv[i] * silu_grad_deep(z[i]);
-  }
+  for (int i = 0; i < V; ++i) p[i] = preact<kBias, V>(w, bv, i, h3[i], h2[i], h1[i], xc[i]);
+  dpre_row<kBf16Policy, V>(p, dyv, lut, dp);
   if (accumulate) {
+    // acc_k += dpre * x[v-3+k] as one fused multiply-add (the product of
+    // two binary32 values is exact in binary64, so under FP64 accumulation
+    // only the sum rounds); acc_4 += dpre.
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < V; ++i) {
       const Acc g = (Acc)dp[i];
-      acc.v[0][i] += g * (Acc)h3[i];
-      acc.v[1][i] += g * (Acc)h2[i];
-      acc.v[2][i] += g * (Acc)h1[i];
-      acc.v[3][i] += g * (Acc)xc[i];
+      acc.v[0][i] = fma_acc(g, (Acc)h3[i], acc.v[0][i]);
+      acc.v[1][i] = fma_acc(g, (Acc)h2[i], acc.v[1][i]);
+      acc.v[2][i] = fma_acc(g, (Acc)h1[i], acc.v[2][i]);
+      acc.v[3][i] = fma_acc(g, (Acc)xc[i], acc.v[3][i]);
       acc.v[4][i] += g;
     }
   }
   if (emit) {
-    // dx[v-3] = w3 d[v-3] + w2 d[v-2] + w1 d[v-1] + w0 d[v], each later
-    // token counted only if no document starts between v-3 and it.
-    const bool m1 = !masked || !(hist & 4u);
-    const bool m2 = !masked || !(hist & 6u);
-    const bool m3 = !masked || !(hist & 7u);
-    float dxv[8];
+    // dx[v-3] = w3 d[v-3] + w2 d[v-2] + w1 d[v-1] + w0 d[v].
+    const bool m1 = !kMasked || !(hist & 4u);
+    const bool m2 = !kMasked || !(hist & 6u);
+    const bool m3 = !kMasked || !(hist & 7u);
+    float dxv[V];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < V; ++i) {
       float s = w[3][i] * d3[i];
       s = __builtin_fmaf(w[2][i], m1 ? d2[i] : 0.0f, s);
       s = __builtin_fmaf(w[1][i], m2 ? d1[i] : 0.0f, s);
       s = __builtin_fmaf(w[0][i], m3 ? dp[i] : 0.0f, s);
       dxv[i] = s;
     }
-    st16(rdx, dx_off, pack8(dxv));
+    Vec<V>::store(rdx, dx_off, pack<V>(dxv));
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < V; ++i) {
     h3[i] = h2[i]; h2[i] = h1[i]; h1[i] = xc[i];
     d3[i] = d2[i]; d2[i] = d1[i]; d1[i] = dp[i];
   }
 }
 
-template <bool kBias, bool kBf16Policy, typename Acc>
+template <bool kBias, bool kBf16Policy, typename Acc, int V>
 __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdArgs a) {
+  typedef Vec<V> VT;
+  __shared__ float lut_lds[kBf16Policy ? 2 * kLutN : 1];
+  if (kBf16Policy) {
+    // Every thread helps to stage the table before any may leave.
+    for (int i = threadIdx.x; i < 2 * kLutN; i += kBlock) lut_lds[i] = kSiluGradTable.v[i];
+    __syncthreads();
+  }
   Lane L;
-  if (!lane_coords(a.nvec, a.rows, a.bands, a.C, L)) return;
+  if (!lane_coords<V>(a.nvec, a.rows, a.bands, a.C, L)) return;
   const int32_t row_bytes = a.C * 2;
   const uint32_t nrec = span_bytes(a.S, a.C, L.base_row);
   const int64_t base_elt = (int64_t)L.base_row * a.C;
@@ -427,15 +580,15 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdArgs a) {
   const rsrc_t rdy = make_rsrc(a.dy + base_elt, nrec);
   const rsrc_t rdx = make_rsrc(a.dx + base_elt, nrec);
 
-  float w[4][8], bv[8];
-  load_weights(a.w, a.w_bf16, L.vec * kVec, w);
-  if (kBias) load_bias(a.b, a.b_bf16, L.vec * kVec, bv);
+  float w[4][V], bv[V];
+  load_weights<V>(a.w, a.w_bf16, L.vec * V, w);
+  if (kBias) load_bias<V>(a.b, a.b_bf16, L.vec * V, bv);
 
-  Partials<Acc> acc;
+  Partials<Acc, V> acc;
 #pragma unroll
   for (int k = 0; k < 5; ++k)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc.v[k][i] = (Acc)0;
+    for (int i = 0; i < V; ++i) acc.v[k][i] = (Acc)0;
 
   int32_t r = L.t0 - 3;
   int32_t off = L.off;
@@ -443,71 +596,81 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdArgs a) {
   walk.init(a.cu, a.num_docs, max(r, 0));
   uint32_t hist = 0;  // bit 0 = row r-1 starts a document, bit 1 = row r-2
 
-  float h1[8], h2[8], h3[8], d1[8], d2[8], d3[8];
+  float h1[V], h2[V], h3[V], d1[V], d2[V], d3[V];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) h1[i] = h2[i] = h3[i] = d1[i] = d2[i] = d3[i] = 0.0f;
+  for (int i = 0; i < V; ++i) h1[i] = h2[i] = h3[i] = d1[i] = d2[i] = d3[i] = 0.0f;
 
   // Halo rows t0-3 .. t0-1: x only.
 #pragma unroll
   for (int q = 0; q < 3; ++q, ++r, off += row_bytes) {
-    u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-    if (r >= 0) v = ld16(rx, off);
+    typename VT::raw v = VT::zero();
+    if (r >= 0) v = VT::load(rx, off);
     uint32_t start = 0;
     if (r == walk.next) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) h1[i] = h2[i] = 0.0f;
+      for (int i = 0; i < V; ++i) h1[i] = h2[i] = 0.0f;
       walk.advance(r);
       start = 1;
     }
     hist = ((hist << 1) | start) & 3u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) h3[i] = h2[i], h2[i] = h1[i];
-    unpack8(v, h1);
+    for (int i = 0; i < V; ++i) h3[i] = h2[i], h2[i] = h1[i];
+    unpack<V>(v, h1);
   }
 
   // Band rows t0 .. t0+T-1 (partials), then three look-ahead rows (dx only).
   const int32_t total = a.rows + 3;
   for (int32_t done = 0; done < total; done += kBwdGroup) {
-    u32x4 xr[kBwdGroup], dr[kBwdGroup];
+    typename VT::raw xr[kBwdGroup], dr[kBwdGroup];
 #pragma unroll
     for (int g = 0; g < kBwdGroup; ++g) {
-      xr[g] = ld16(rx, off + g * row_bytes);
-      dr[g] = ld16(rdy, off + g * row_bytes);
+      xr[g] = VT::load(rx, off + g * row_bytes);
+      dr[g] = VT::load(rdy, off + g * row_bytes);
     }
-    const bool quiet = hist == 0 && walk.next > r + (kBwdGroup - 1);
+    if (hist == 0 && walk.next > r + (kBwdGroup - 1)) {
+      // No document starts in rows r-2 .. r+G-1: no resets, no masks.
 #pragma unroll
-    for (int g = 0; g < kBwdGroup; ++g) {
-      const int32_t idx = done + g;        // row t0 + idx
-      if (idx >= total) break;
-      uint32_t h3bits = 0;
-      if (!quiet) {
+      for (int g = 0; g < kBwdGroup; ++g) {
+        const int32_t idx = done + g;  // row t0 + idx
+        if (idx >= total) break;
+        float xc[V];
+        unpack<V>(xr[g], xc);
+        bwd_row<kBias, kBf16Policy, false, Acc, V>(w, bv, lut_lds, xc, dr[g], h1, h2, h3, d1, d2,
+                                                   d3, acc, idx < a.rows, idx >= 3, 0u, rdx,
+                                                   off + (g - 3) * row_bytes);
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < kBwdGroup; ++g) {
+        const int32_t idx = done + g;
+        if (idx >= total) break;
         uint32_t start = 0;
         if (r + g == walk.next) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) h1[i] = h2[i] = h3[i] = 0.0f;
+          for (int i = 0; i < V; ++i) h1[i] = h2[i] = h3[i] = 0.0f;
           walk.advance(r + g);
           start = 1;
         }
-        h3bits = (hist << 1) | start;
+        const uint32_t h3bits = (hist << 1) | start;
         hist = h3bits & 3u;
+        float xc[V];
+        unpack<V>(xr[g], xc);
+        bwd_row<kBias, kBf16Policy, true, Acc, V>(w, bv, lut_lds, xc, dr[g], h1, h2, h3, d1, d2,
+                                                  d3, acc, idx < a.rows, idx >= 3, h3bits, rdx,
+                                                  off + (g - 3) * row_bytes);
       }
-      float xc[8];
-      unpack8(xr[g], xc);
-      bwd_row<kBias, kBf16Policy, Acc>(w, bv, xc, dr[g], h1, h2, h3, d1, d2, d3, acc,
-                                       idx < a.rows, idx >= 3, h3bits, !quiet, rdx,
-                                       off + (g - 3) * row_bytes);
     }
     r += kBwdGroup;
     off += kBwdGroup * row_bytes;
   }
 
   // One partial row per band: part[band][k][c].
-  Acc* part = reinterpret_cast<Acc*>(a.part) + (int64_t)L.band * 5 * a.C + L.vec * kVec;
+  Acc* part = reinterpret_cast<Acc*>(a.part) + (int64_t)L.band * 5 * a.C + L.vec * V;
 #pragma unroll
   for (int k = 0; k < 5; ++k) {
     Acc* dst = part + (int64_t)k * a.C;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = acc.v[k][i];
+    for (int i = 0; i < V; ++i) dst[i] = acc.v[k][i];
   }
 }
 
@@ -559,28 +722,40 @@ __global__ __launch_bounds__(kRedOut * kRedChunks) void bwd_reduce_kernel(Reduce
   }
 }
 
+template <int V>
+hipError_t launch_fwd_v(const Plan& plan, const FwdArgs& a, bool has_bias, hipStream_t s) {
+  dim3 grid(plan.blocks), block(kBlock);
+  if (has_bias) hipLaunchKernelGGL((fwd_kernel<true, V>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((fwd_kernel<false, V>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int V>
+hipError_t launch_bwd_main_v(const Plan& plan, const BwdArgs& a, bool has_bias, bool fp32_policy,
+                             hipStream_t s) {
+  dim3 grid(plan.blocks), block(kBlock);
+  if (fp32_policy) {
+    if (has_bias) hipLaunchKernelGGL((bwd_main_kernel<true, false, double, V>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((bwd_main_kernel<false, false, double, V>), grid, block, 0, s, a);
+  } else {
+    if (has_bias) hipLaunchKernelGGL((bwd_main_kernel<true, true, float, V>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((bwd_main_kernel<false, true, float, V>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // ============================================================ launchers ==
 
 hipError_t launch_fwd(const Plan& plan, const FwdArgs& a, bool has_bias, hipStream_t s) {
-  dim3 grid(plan.blocks), block(kBlock);
-  if (has_bias) hipLaunchKernelGGL(fwd_kernel<true>, grid, block, 0, s, a);
-  else hipLaunchKernelGGL(fwd_kernel<false>, grid, block, 0, s, a);
-  return hipGetLastError();
+  return plan.vec == 8 ? launch_fwd_v<8>(plan, a, has_bias, s) : launch_fwd_v<4>(plan, a, has_bias, s);
 }
 
 hipError_t launch_bwd_main(const Plan& plan, const BwdArgs& a, bool has_bias, bool fp32_policy,
                            hipStream_t s) {
-  dim3 grid(plan.blocks), block(kBlock);
-  if (fp32_policy) {
-    if (has_bias) hipLaunchKernelGGL((bwd_main_kernel<true, false, double>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((bwd_main_kernel<false, false, double>), grid, block, 0, s, a);
-  } else {
-    if (has_bias) hipLaunchKernelGGL((bwd_main_kernel<true, true, float>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((bwd_main_kernel<false, true, float>), grid, block, 0, s, a);
-  }
-  return hipGetLastError();
+  return plan.vec == 8 ? launch_bwd_main_v<8>(plan, a, has_bias, fp32_policy, s)
+                       : launch_bwd_main_v<4>(plan, a, has_bias, fp32_policy, s);
 }
 
 hipError_t launch_bwd_reduce(const Plan& plan, const ReduceArgs& a, bool fp64, hipStream_t s) {
