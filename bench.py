@@ -26,7 +26,7 @@ if ROOT not in sys.path:
 METRIC = "fwd/bwd HBM GB/s + Mtokens/s, S=64K C=4096 packed; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = "headline"
-CPU_SAMPLE_CHANNELS = 2048
+CPU_SAMPLE_CHANNELS = 4096
 
 
 def algorithmic_bytes(wl, direction):

@@ -7,6 +7,7 @@
 
 #include "vdc.h"
 
+#include <algorithm>
 #include <atomic>
 #include <stdint.h>
 
@@ -19,9 +20,6 @@ std::atomic<uint64_t> g_launches{0};
 
 constexpr int64_t kMaxC = int64_t(1) << 20;
 constexpr int64_t kMaxS = (int64_t(1) << 31) - 1;
-// Lanes that keep the whole chip busy at the occupancy these kernels reach
-// (256 CUs x 16 wave64).
-constexpr int64_t kFillLanes = 256 * 16 * 64;
 // Smallest lane vector: the size checks below are made for it.
 constexpr int64_t kMinVec = 4;
 
@@ -44,20 +42,19 @@ int64_t wave_span_rows(int64_t nvec, int64_t rows) {
   return (ceil_div(64, nvec) + 1) * rows + 8;
 }
 
-// Tokens per band.  Forward: 64 (halo re-read 3/64 of x), fewer when the
-// problem is too small to fill the chip.  Backward: 256, more for large
-// problems (fewer partial rows) and fewer for small ones.  A function of
-// (direction, S, C) only.
+// Tokens per band, a power of two in [max(16, G), 1024]: the one whose wave count
+// (bands * C/V / 64) is nearest to the direction's target (see
+// vdc_internal.h), then lowered while one wave's span of rows would not fit
+// 32-bit offsets.  A function of (direction, S, C) only.
 int32_t pick_vec(int dir) { return dir == VDC_FWD ? kFwdVec : kBwdVec; }
 
 int32_t pick_rows(int dir, int64_t S, int64_t C) {
   const int64_t nvec = C / pick_vec(dir);
-  int64_t rows = dir == VDC_FWD ? 64 : 256;
-  const int64_t lo = 16;
-  auto lanes = [&](int64_t r) { return ceil_div(S, r) * nvec; };
-  while (rows > lo && lanes(rows) < kFillLanes) rows /= 2;
-  if (dir == VDC_BWD)
-    while (rows < 1024 && lanes(rows * 2) >= 2 * kFillLanes) rows *= 2;
+  const double target = dir == VDC_FWD ? kFwdTargetWaves : kBwdTargetWaves;
+  auto waves = [&](int64_t r) { return double(ceil_div(S, r) * nvec) / 64.0; };
+  const int64_t lo = std::max<int64_t>(16, dir == VDC_FWD ? kFwdGroup : kBwdGroup);
+  int64_t rows = lo;
+  while (rows < 1024 && waves(rows * 2) >= target / 1.41421356) rows *= 2;
   while (rows > lo && wave_span_rows(nvec, rows) * C * 2 >= (int64_t(1) << 31)) rows /= 2;
   return (int32_t)rows;
 }

@@ -16,13 +16,30 @@ namespace vdc {
 #ifndef VDC_BWD_VEC
 #define VDC_BWD_VEC 4
 #endif
+// Wave count the planner aims at: few, long-running waves with many rows
+// in flight each stream better than many short ones (measured on MI355X:
+// 256 CUs, so 4096 waves = 4 per SIMD, 2048 = 2 per SIMD).
+#ifndef VDC_FWD_TARGET_WAVES
+#define VDC_FWD_TARGET_WAVES 4096
+#endif
+#ifndef VDC_BWD_TARGET_WAVES
+#define VDC_BWD_TARGET_WAVES 2048
+#endif
+constexpr int kFwdTargetWaves = VDC_FWD_TARGET_WAVES;
+constexpr int kBwdTargetWaves = VDC_BWD_TARGET_WAVES;
 constexpr int kFwdVec = VDC_FWD_VEC;
 constexpr int kBwdVec = VDC_BWD_VEC;
 // Threads per workgroup of the main kernels (four wave64).
 constexpr int kBlock = 256;
 // Rows one lane loads ahead and processes as one unrolled group.
-constexpr int kFwdGroup = 8;
-constexpr int kBwdGroup = 4;
+#ifndef VDC_FWD_GROUP
+#define VDC_FWD_GROUP 16
+#endif
+#ifndef VDC_BWD_GROUP
+#define VDC_BWD_GROUP 8
+#endif
+constexpr int kFwdGroup = VDC_FWD_GROUP;
+constexpr int kBwdGroup = VDC_BWD_GROUP;
 // Reduce kernel: outputs per workgroup and row chunks (one wave each).
 constexpr int kRedOut = 64;
 constexpr int kRedChunks = 8;
