@@ -20,8 +20,12 @@ std::atomic<uint64_t> g_launches{0};
 
 constexpr int64_t kMaxC = int64_t(1) << 20;
 constexpr int64_t kMaxS = (int64_t(1) << 31) - 1;
-// Smallest lane vector: the size checks below are made for it.
+// Smallest lane vector and largest row group: the size checks below are
+// made for them.
 constexpr int64_t kMinVec = 4;
+constexpr int64_t kMaxGroup = kFwdGroup > kBwdGroup ? kFwdGroup : kBwdGroup;
+// Compute units of the MI355X; plans are made for it.
+constexpr int64_t kCUs = 256;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -42,27 +46,35 @@ int64_t wave_span_rows(int64_t nvec, int64_t rows) {
   return (ceil_div(64, nvec) + 1) * rows + 8;
 }
 
-// Tokens per band, a power of two in [max(16, G), 1024]: the one whose wave count
-// (bands * C/V / 64) is nearest to the direction's target (see
-// vdc_internal.h), then lowered while one wave's span of rows would not fit
-// 32-bit offsets.  A function of (direction, S, C) only.
+// Tokens per band T.  Every band is one wave's work (64 lanes of C/V
+// channels each), and the kernels are built to run one wave per SIMD with a
+// deep load pipeline, so T is the smallest multiple of 2G for which the
+// bands fit one wave per SIMD of the MI355X (256 CUs x 4 SIMDs): all waves
+// start together and finish together.  Lowered only if one wave's span of
+// rows would not fit 32-bit offsets (C in the hundreds of thousands).
+// A function of (direction, S, C) only.
 int32_t pick_vec(int dir) { return dir == VDC_FWD ? kFwdVec : kBwdVec; }
 
-int32_t pick_rows(int dir, int64_t S, int64_t C) {
+int64_t pick_rows(int dir, int64_t S, int64_t C) {
   const int64_t nvec = C / pick_vec(dir);
-  const double target = dir == VDC_FWD ? kFwdTargetWaves : kBwdTargetWaves;
-  auto waves = [&](int64_t r) { return double(ceil_div(S, r) * nvec) / 64.0; };
-  const int64_t lo = std::max<int64_t>(16, dir == VDC_FWD ? kFwdGroup : kBwdGroup);
-  int64_t rows = lo;
-  while (rows < 1024 && waves(rows * 2) >= target / 1.41421356) rows *= 2;
-  while (rows > lo && wave_span_rows(nvec, rows) * C * 2 >= (int64_t(1) << 31)) rows /= 2;
-  return (int32_t)rows;
+  const int64_t step = 2 * (dir == VDC_FWD ? kFwdGroup : kBwdGroup);
+  const int64_t lanes_cap = kCUs * 4 * (dir == VDC_FWD ? kFwdWaves : kBwdWaves) * 64;
+  const int64_t bands_cap = std::max<int64_t>(1, lanes_cap / nvec);
+  int64_t rows = std::max<int64_t>(step, ceil_div(ceil_div(std::max<int64_t>(S, 1), bands_cap), step) * step);
+  while (rows > step && wave_span_rows(nvec, rows) * C * 2 >= (int64_t(1) << 31)) rows -= step;
+#ifdef VDC_ROWS_FORCE_FWD
+  if (dir == VDC_FWD) rows = VDC_ROWS_FORCE_FWD;
+#endif
+#ifdef VDC_ROWS_FORCE_BWD
+  if (dir == VDC_BWD) rows = VDC_ROWS_FORCE_BWD;
+#endif
+  return rows;
 }
 
 Plan make_plan(int dir, int64_t S, int64_t C, int policy) {
   Plan p{};
   p.vec = pick_vec(dir);
-  p.rows = pick_rows(dir, S, C);
+  p.rows = (int32_t)pick_rows(dir, S, C);
   p.bands = (int32_t)ceil_div(S, p.rows);
   p.lanes = (int64_t)p.bands * (C / p.vec);
   p.blocks = (int32_t)ceil_div(p.lanes, kBlock);
@@ -78,7 +90,7 @@ int check_sizes(int64_t S, int64_t C, int64_t num_docs) {
   if (num_docs < 0 || num_docs > kMaxS - 1) return VDC_EINVAL;
   if (S > 0 && num_docs < 1) return VDC_EINVAL;
   // The planner must find a band size whose wave span fits 32-bit offsets.
-  if (wave_span_rows(C / kMinVec, 16) * C * 2 >= (int64_t(1) << 31)) return VDC_EINVAL;
+  if (wave_span_rows(C / kMinVec, 2 * kMaxGroup) * C * 2 >= (int64_t(1) << 31)) return VDC_EINVAL;
   return VDC_OK;
 }
 

@@ -16,22 +16,21 @@ namespace vdc {
 #ifndef VDC_BWD_VEC
 #define VDC_BWD_VEC 4
 #endif
-// Wave count the planner aims at: few, long-running waves with many rows
-// in flight each stream better than many short ones (measured on MI355X:
-// 256 CUs, so 4096 waves = 4 per SIMD, 2048 = 2 per SIMD).
-#ifndef VDC_FWD_TARGET_WAVES
-#define VDC_FWD_TARGET_WAVES 4096
+// Waves per SIMD each kernel is built for (register budget) and planned
+// for: one, with a deep double-buffered load pipeline per wave.
+#ifndef VDC_FWD_WAVES
+#define VDC_FWD_WAVES 1
 #endif
-#ifndef VDC_BWD_TARGET_WAVES
-#define VDC_BWD_TARGET_WAVES 2048
+#ifndef VDC_BWD_WAVES
+#define VDC_BWD_WAVES 1
 #endif
-constexpr int kFwdTargetWaves = VDC_FWD_TARGET_WAVES;
-constexpr int kBwdTargetWaves = VDC_BWD_TARGET_WAVES;
+constexpr int kFwdWaves = VDC_FWD_WAVES;
+constexpr int kBwdWaves = VDC_BWD_WAVES;
 constexpr int kFwdVec = VDC_FWD_VEC;
 constexpr int kBwdVec = VDC_BWD_VEC;
 // Threads per workgroup of the main kernels (four wave64).
 constexpr int kBlock = 256;
-// Rows one lane loads ahead and processes as one unrolled group.
+// Rows per load group (two groups are in flight per lane).
 #ifndef VDC_FWD_GROUP
 #define VDC_FWD_GROUP 16
 #endif

@@ -398,7 +398,8 @@ __device__ __forceinline__ typename Vec<V>::raw fwd_row(const float (&w)[4][V],
 }
 
 template <bool kBias, int V>
-__global__ __launch_bounds__(kBlock) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kFwdWaves)))
+void fwd_kernel(FwdArgs a) {
   typedef Vec<V> VT;
   Lane L;
   if (!lane_coords<V>(a.nvec, a.rows, a.bands, a.C, L)) return;
@@ -436,17 +437,23 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(FwdArgs a) {
     unpack<V>(v, h1);
   }
 
-  for (int32_t done = 0; done < a.rows; done += kFwdGroup) {
-    typename VT::raw raw[kFwdGroup];
+  // Groups of G rows, two register buffers: the loads of group k+1 are in
+  // flight while group k is computed; a group's y rows are stored together
+  // after its last row (loads and stores share one wait counter on this
+  // architecture, so a store between loads would stall the next wait).
+  typedef typename VT::raw Raw;
+  auto load = [&](Raw (&buf)[kFwdGroup], int32_t at) {
 #pragma unroll
-    for (int g = 0; g < kFwdGroup; ++g) raw[g] = VT::load(rx, off + g * row_bytes);
+    for (int g = 0; g < kFwdGroup; ++g) buf[g] = VT::load(rx, at + g * row_bytes);
+  };
+  auto run = [&](Raw (&buf)[kFwdGroup]) {
     if (walk.next > r + (kFwdGroup - 1)) {
       // No document starts in this group.
 #pragma unroll
       for (int g = 0; g < kFwdGroup; ++g) {
         float xc[V];
-        unpack<V>(raw[g], xc);
-        VT::store(ry, off + g * row_bytes, fwd_row<kBias, V>(w, bv, h3, h2, h1, xc));
+        unpack<V>(buf[g], xc);
+        buf[g] = fwd_row<kBias, V>(w, bv, h3, h2, h1, xc);
 #pragma unroll
         for (int i = 0; i < V; ++i) h3[i] = h2[i], h2[i] = h1[i], h1[i] = xc[i];
       }
@@ -459,14 +466,25 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(FwdArgs a) {
           walk.advance(r + g);
         }
         float xc[V];
-        unpack<V>(raw[g], xc);
-        VT::store(ry, off + g * row_bytes, fwd_row<kBias, V>(w, bv, h3, h2, h1, xc));
+        unpack<V>(buf[g], xc);
+        buf[g] = fwd_row<kBias, V>(w, bv, h3, h2, h1, xc);
 #pragma unroll
         for (int i = 0; i < V; ++i) h3[i] = h2[i], h2[i] = h1[i], h1[i] = xc[i];
       }
     }
+#pragma unroll
+    for (int g = 0; g < kFwdGroup; ++g) VT::store(ry, off + g * row_bytes, buf[g]);
     r += kFwdGroup;
     off += kFwdGroup * row_bytes;
+  };
+  // T is a multiple of 2G (host rule).
+  Raw A[kFwdGroup], B[kFwdGroup];
+  load(A, off);
+  for (int32_t done = 0; done < a.rows; done += 2 * kFwdGroup) {
+    load(B, off + kFwdGroup * row_bytes);
+    run(A);
+    if (done + 2 * kFwdGroup < a.rows) load(A, off + kFwdGroup * row_bytes);
+    run(B);
   }
 }
 
@@ -518,8 +536,8 @@ __device__ __forceinline__ void bwd_row(const float (&w)[4][V], const float (&bv
                                         typename Vec<V>::raw dyraw, float (&h1)[V],
                                         float (&h2)[V], float (&h3)[V], float (&d1)[V],
                                         float (&d2)[V], float (&d3)[V], Partials<Acc, V>& acc,
-                                        bool accumulate, bool emit, uint32_t hist, rsrc_t rdx,
-                                        int32_t dx_off) {
+                                        bool accumulate, bool emit, uint32_t hist,
+                                        typename Vec<V>::raw& dx_out) {
   float dyv[V], p[V], dp[V];
   unpack<V>(dyraw, dyv);
 #pragma unroll
@@ -553,7 +571,7 @@ __device__ __forceinline__ void bwd_row(const float (&w)[4][V], const float (&bv
       s = __builtin_fmaf(w[0][i], m3 ? dp[i] : 0.0f, s);
       dxv[i] = s;
     }
-    Vec<V>::store(rdx, dx_off, pack<V>(dxv));
+    dx_out = pack<V>(dxv);
   }
 #pragma unroll
   for (int i = 0; i < V; ++i) {
@@ -563,7 +581,8 @@ __device__ __forceinline__ void bwd_row(const float (&w)[4][V], const float (&bv
 }
 
 template <bool kBias, bool kBf16Policy, typename Acc, int V>
-__global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kBwdWaves)))
+void bwd_main_kernel(BwdArgs a) {
   typedef Vec<V> VT;
   __shared__ float lut_lds[kBf16Policy ? 2 * kLutN : 1];
   if (kBf16Policy) {
@@ -618,32 +637,40 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdArgs a) {
     unpack<V>(v, h1);
   }
 
-  // Band rows t0 .. t0+T-1 (partials), then three look-ahead rows (dx only).
-  const int32_t total = a.rows + 3;
-  for (int32_t done = 0; done < total; done += kBwdGroup) {
-    typename VT::raw xr[kBwdGroup], dr[kBwdGroup];
+  // Band rows t0 .. t0+T-1 (partials) in groups of G with two register
+  // buffers: the loads of group k+1 are in flight while group k is
+  // computed, and a group's dx rows are stored together after its last row
+  // (loads and stores share one wait counter on this architecture).  Row
+  // t0+idx emits dx of row t0+idx-3, so the band's first three rows emit
+  // nothing and three look-ahead rows, loaded during the last group,
+  // finish the band.
+  typedef typename VT::raw Raw;
+  auto load = [&](Raw (&xr)[kBwdGroup], Raw (&dr)[kBwdGroup], int32_t at, int nrows) {
 #pragma unroll
     for (int g = 0; g < kBwdGroup; ++g) {
-      xr[g] = VT::load(rx, off + g * row_bytes);
-      dr[g] = VT::load(rdy, off + g * row_bytes);
+      if (g < nrows) {
+        xr[g] = VT::load(rx, at + g * row_bytes);
+        dr[g] = VT::load(rdy, at + g * row_bytes);
+      }
     }
-    if (hist == 0 && walk.next > r + (kBwdGroup - 1)) {
-      // No document starts in rows r-2 .. r+G-1: no resets, no masks.
+  };
+  auto run = [&](Raw (&xr)[kBwdGroup], Raw (&dr)[kBwdGroup], int32_t done, int nrows,
+                 bool accumulate) {
+    if (hist == 0 && walk.next > r + (nrows - 1)) {
+      // No document starts in rows r-2 .. r+nrows-1: no resets, no masks.
 #pragma unroll
       for (int g = 0; g < kBwdGroup; ++g) {
-        const int32_t idx = done + g;  // row t0 + idx
-        if (idx >= total) break;
+        if (g >= nrows) break;
         float xc[V];
         unpack<V>(xr[g], xc);
         bwd_row<kBias, kBf16Policy, false, Acc, V>(w, bv, lut_lds, xc, dr[g], h1, h2, h3, d1, d2,
-                                                   d3, acc, idx < a.rows, idx >= 3, 0u, rdx,
-                                                   off + (g - 3) * row_bytes);
+                                                   d3, acc, accumulate, done + g >= 3, 0u,
+                                                   xr[g]);
       }
     } else {
 #pragma unroll
       for (int g = 0; g < kBwdGroup; ++g) {
-        const int32_t idx = done + g;
-        if (idx >= total) break;
+        if (g >= nrows) break;
         uint32_t start = 0;
         if (r + g == walk.next) {
 #pragma unroll
@@ -656,13 +683,27 @@ __global__ __launch_bounds__(kBlock) void bwd_main_kernel(BwdArgs a) {
         float xc[V];
         unpack<V>(xr[g], xc);
         bwd_row<kBias, kBf16Policy, true, Acc, V>(w, bv, lut_lds, xc, dr[g], h1, h2, h3, d1, d2,
-                                                  d3, acc, idx < a.rows, idx >= 3, h3bits, rdx,
-                                                  off + (g - 3) * row_bytes);
+                                                  d3, acc, accumulate, done + g >= 3, h3bits,
+                                                  xr[g]);
       }
     }
-    r += kBwdGroup;
-    off += kBwdGroup * row_bytes;
+    // xr[g] now holds the packed dx of row r+g-3.
+#pragma unroll
+    for (int g = 0; g < kBwdGroup; ++g)
+      if (g < nrows && done + g >= 3) VT::store(rdx, off + (g - 3) * row_bytes, xr[g]);
+    r += nrows;
+    off += nrows * row_bytes;
+  };
+  // T is a multiple of 2G (host rule).
+  Raw xa[kBwdGroup], da[kBwdGroup], xb[kBwdGroup], db[kBwdGroup];
+  load(xa, da, off, kBwdGroup);
+  for (int32_t done = 0; done < a.rows; done += 2 * kBwdGroup) {
+    load(xb, db, off + kBwdGroup * row_bytes, kBwdGroup);
+    run(xa, da, done, kBwdGroup, true);
+    load(xa, da, off + kBwdGroup * row_bytes, done + 2 * kBwdGroup < a.rows ? kBwdGroup : 3);
+    run(xb, db, done + kBwdGroup, kBwdGroup, true);
   }
+  run(xa, da, a.rows, 3, false);
 
   // One partial row per band: part[band][k][c].
   Acc* part = reinterpret_cast<Acc*>(a.part) + (int64_t)L.band * 5 * a.C + L.vec * V;
