@@ -149,7 +149,8 @@ def test_workspace_bytes(lib):
 
 def test_plans_depend_on_shape_only(lib):
     for d in (FWD, BWD):
-        for S, C in ((65536, 4096), (262144, 520), (1000, 64)):
+        for S, C in ((65536, 4096), (262144, 520), (1000, 64), (2 ** 31 - 1, 8),
+                     (2 ** 27, 8), (2 ** 24, 24), (2 ** 20, 2 ** 20), (5, 8)):
             a, b = (ctypes.c_int64 * 10)(), (ctypes.c_int64 * 10)()
             assert lib.conv1d_plan(d, S, C, 0, a) == OK
             assert lib.conv1d_plan(d, S, C, 0, b) == OK
@@ -161,6 +162,11 @@ def test_plans_depend_on_shape_only(lib):
             # a wave's span of rows stays far inside 32-bit byte offsets
             span = (-(-64 // (C // vec)) + 1) * rows + 8
             assert span * C * 2 < 2 ** 31
+            # a workgroup's rows (its bands and 3 halo rows on each side)
+            # fit its 1024-word LDS bitmask of document starts
+            block_rows = (-(-threads // (C // vec)) + 1) * rows + 6
+            assert block_rows < 32 * 1023
+            assert bands * rows >= S and (bands - 1) * rows < max(S, 1)
 
 
 def test_status_strings(lib):

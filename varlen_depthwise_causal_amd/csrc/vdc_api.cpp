@@ -46,12 +46,24 @@ int64_t wave_span_rows(int64_t nvec, int64_t rows) {
   return (ceil_div(64, nvec) + 1) * rows + 8;
 }
 
+// Largest span, in rows, of one workgroup: the bands of its kBlock lanes
+// plus three halo rows on each side.  Its document starts must fit the
+// workgroup's LDS bitmask.
+int64_t block_span_rows(int64_t nvec, int64_t rows) {
+  return (ceil_div(kBlock, nvec) + 1) * rows + 6;
+}
+bool block_fits(int64_t nvec, int64_t rows) {
+  return block_span_rows(nvec, rows) < 32 * (int64_t)(kDocMaskWords - 1);
+}
+
 // Tokens per band T.  Every band is one wave's work (64 lanes of C/V
 // channels each), and the kernels are built to run one wave per SIMD with a
 // deep load pipeline, so T is the smallest multiple of 2G for which the
 // bands fit one wave per SIMD of the MI355X (256 CUs x 4 SIMDs): all waves
-// start together and finish together.  Lowered only if one wave's span of
-// rows would not fit 32-bit offsets (C in the hundreds of thousands).
+// start together and finish together.  Lowered if one wave's span of rows
+// would not fit 32-bit offsets (C in the hundreds of thousands) or one
+// workgroup's rows would not fit its document-start bitmask (small C with
+// very long S); then there are more bands than SIMDs.
 // A function of (direction, S, C) only.
 int32_t pick_vec(int dir) { return dir == VDC_FWD ? kFwdVec : kBwdVec; }
 
@@ -61,7 +73,9 @@ int64_t pick_rows(int dir, int64_t S, int64_t C) {
   const int64_t lanes_cap = kCUs * 4 * (dir == VDC_FWD ? kFwdWaves : kBwdWaves) * 64;
   const int64_t bands_cap = std::max<int64_t>(1, lanes_cap / nvec);
   int64_t rows = std::max<int64_t>(step, ceil_div(ceil_div(std::max<int64_t>(S, 1), bands_cap), step) * step);
-  while (rows > step && wave_span_rows(nvec, rows) * C * 2 >= (int64_t(1) << 31)) rows -= step;
+  while (rows > step && (wave_span_rows(nvec, rows) * C * 2 >= (int64_t(1) << 31) ||
+                         !block_fits(nvec, rows)))
+    rows -= step;
 #ifdef VDC_ROWS_FORCE_FWD
   if (dir == VDC_FWD) rows = VDC_ROWS_FORCE_FWD;
 #endif
@@ -91,6 +105,8 @@ int check_sizes(int64_t S, int64_t C, int64_t num_docs) {
   if (S > 0 && num_docs < 1) return VDC_EINVAL;
   // The planner must find a band size whose wave span fits 32-bit offsets.
   if (wave_span_rows(C / kMinVec, 2 * kMaxGroup) * C * 2 >= (int64_t(1) << 31)) return VDC_EINVAL;
+  static_assert((kBlock / 2 + 2) * 2 * kMaxGroup + 6 < 32 * (kDocMaskWords - 1),
+                "the smallest band must fit the document-start bitmask at C = 8");
   return VDC_OK;
 }
 

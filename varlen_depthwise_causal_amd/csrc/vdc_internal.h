@@ -40,6 +40,11 @@ constexpr int kBlock = 256;
 constexpr int kFwdGroup = VDC_FWD_GROUP;
 constexpr int kBwdGroup = VDC_BWD_GROUP;
 // Reduce kernel: outputs per workgroup and row chunks (one wave each).
+// Document-start bitmask of one workgroup, in 32-bit LDS words: the rows a
+// workgroup touches (its bands and three halo rows on each side) must span
+// fewer than 32 * (kDocMaskWords - 1) rows.
+constexpr int kDocMaskWords = 1024;
+
 constexpr int kRedOut = 64;
 constexpr int kRedChunks = 8;
 

@@ -120,7 +120,7 @@ __device__ __forceinline__ void unpack(typename Vec<V>::raw v, float (&f)[V]) {
 
 template <int V>
 __device__ __forceinline__ typename Vec<V>::raw pack(const float (&f)[V]) {
-  typename Vec<V>::raw r;
+  typename Vec<V>::raw r = Vec<V>::zero();
 #pragma unroll
   for (int d = 0; d < V / 2; ++d) r[d] = pack2(f[2 * d], f[2 * d + 1]);
   return r;
@@ -195,35 +195,79 @@ __device__ __forceinline__ void load_bias(const void* b, int bf16, uint32_t c0, 
 }
 
 // ------------------------------------------------- document starts --
+//
+// A row t is a document start when t equals a value of cu_seqlens below S
+// (an empty document repeats its successor's start).  Each workgroup marks
+// the starts among the rows its lanes touch in an LDS bitmask: its first
+// wave finds the range of cu_seqlens entries with two 64-ary searches and
+// the whole workgroup sets the bits.  A lane then reads the starts of a
+// group of rows with two LDS loads, however many documents it holds.
+// The host sizes bands so that a workgroup's rows fit the bitmask.
 
-// The document starts are the values of cu_seqlens below S (an empty
-// document repeats its successor's start).  A lane finds the first start at
-// or after its first row with a binary search and then walks forward.
-struct DocWalk {
-  const int32_t* cu;
-  int32_t last;  // index of the last entry (num_docs)
-  int32_t idx;
-  int32_t next;  // smallest start >= the current row (INT_MAX if none)
+// First index i in [0, n) with cu[i] >= v (n if none), by a whole wave:
+// each round probes 64 evenly spaced entries and keeps the bracket, so the
+// range shrinks 64-fold per dependent load.  Terminates for any contents.
+__device__ __forceinline__ int32_t wave_lower_bound(const int32_t* cu, int32_t n, int32_t v) {
+  const int32_t lane = threadIdx.x & 63;
+  int32_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int32_t step = (hi - lo + 63) >> 6;
+    const int32_t idx = lo + lane * step;
+    const bool less = idx < hi && cu[idx] < v;
+    const uint64_t ball = __ballot(less);
+    const int32_t c = ~ball == 0 ? 64 : (int32_t)__builtin_ctzll(~ball);
+    const int32_t nlo = c == 0 ? lo : lo + (c - 1) * step + 1;
+    hi = min(hi, lo + c * step);
+    lo = nlo;
+  }
+  return lo;
+}
 
-  __device__ __forceinline__ void init(const int32_t* cu_, int32_t num_docs, int32_t row) {
-    cu = cu_;
-    last = num_docs;
-    int32_t lo = 0, hi = num_docs + 1;
-    while (lo < hi) {
-      int32_t mid = (lo + hi) >> 1;
-      if (cu[mid] < row) lo = mid + 1; else hi = mid;
-    }
-    idx = lo;
-    next = lo <= last ? cu[lo] : INT_MAX;
-  }
-  // Called on the row that equals `next`: move past every start <= row.
-  __device__ __forceinline__ void advance(int32_t row) {
-    do {
-      ++idx;
-      next = idx <= last ? cu[idx] : INT_MAX;
-    } while (next <= row);
-  }
+struct DocMask {
+  uint32_t bits[kDocMaskWords + 1];  // bit j: row row_lo + j starts a document
+  int32_t row_lo;
+  int32_t idx_lo, idx_hi;            // cu_seqlens entries that fall in the rows
 };
+
+// Every thread of the workgroup must call this (two barriers).  The rows
+// touched are the workgroup's bands plus three halo rows on each side.
+__device__ __forceinline__ void build_doc_mask(DocMask& m, const int32_t* cu, int32_t num_docs,
+                                               int32_t nvec, int32_t rows, int32_t bands) {
+  const int32_t g0 = (int32_t)blockIdx.x * kBlock;
+  const int32_t first_band = g0 / nvec;
+  const int32_t last_band = min((g0 + kBlock - 1) / nvec, bands - 1);
+  const int32_t row_lo = first_band * rows - 3;
+  const int32_t row_hi = (last_band + 1) * rows + 3;
+  // At most kDocMaskWords + 1 words by the host's choice of rows.
+  const int32_t nwords = ((row_hi - row_lo) >> 5) + 2;
+  for (int32_t i = threadIdx.x; i < nwords; i += kBlock) m.bits[i] = 0u;
+  if (threadIdx.x < 64) {
+    const int32_t lo = wave_lower_bound(cu, num_docs + 1, max(row_lo, 0));
+    const int32_t hi = wave_lower_bound(cu, num_docs + 1, row_hi);
+    if (threadIdx.x == 0) {
+      m.row_lo = row_lo;
+      m.idx_lo = lo;
+      m.idx_hi = hi;
+    }
+  }
+  __syncthreads();
+  const int32_t first_row = max(row_lo, 0);
+  for (int32_t i = m.idx_lo + (int32_t)threadIdx.x; i < m.idx_hi; i += kBlock) {
+    const int32_t t = cu[i];
+    if (t >= first_row && t < row_hi)
+      atomicOr(&m.bits[(t - row_lo) >> 5], 1u << ((t - row_lo) & 31));
+  }
+  __syncthreads();
+}
+
+// Bit g set: row r+g starts a document (1 <= n <= 32, row_lo <= r and
+// r + n <= row_hi of the workgroup).
+__device__ __forceinline__ uint32_t doc_starts(const DocMask& m, int32_t r, int n) {
+  const int32_t b = r - m.row_lo;
+  const uint32_t bits =
+      __builtin_amdgcn_alignbit(m.bits[(b >> 5) + 1], m.bits[b >> 5], (uint32_t)b & 31u);
+  return n >= 32 ? bits : bits & ((1u << n) - 1u);
+}
 
 // ------------------------------------------------------ SiLU pieces --
 
@@ -352,14 +396,19 @@ template <int V>
 __device__ __forceinline__ bool lane_coords(int32_t nvec, int32_t rows, int32_t bands, int32_t C,
                                             Lane& L) {
   const uint32_t g = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
-  L.band = g / (uint32_t)nvec;
-  if (L.band >= (uint32_t)bands) return false;
-  L.vec = g - L.band * (uint32_t)nvec;
+  const uint32_t band = g / (uint32_t)nvec;
+  const bool active = band < (uint32_t)bands;
+  // Lanes past the last band keep the last band's coordinates (they load
+  // and store nothing) so that every address below stays meaningful.
+  L.band = active ? band : (uint32_t)bands - 1u;
+  L.vec = active ? g - band * (uint32_t)nvec : 0u;
   L.t0 = (int32_t)L.band * rows;
+  // The wave's base row comes from its first lane, which has the smallest
+  // band of the wave.
   const int32_t first_band = __builtin_amdgcn_readfirstlane((int32_t)L.band);
   L.base_row = max(first_band * rows - 3, 0);
   L.off = (L.t0 - 3 - L.base_row) * (C * 2) + (int32_t)L.vec * (V * 2);
-  return true;
+  return active;
 }
 
 // ===================================================== forward kernel ==
@@ -401,85 +450,97 @@ template <bool kBias, int V>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kFwdWaves)))
 void fwd_kernel(FwdArgs a) {
   typedef Vec<V> VT;
+  typedef typename VT::raw Raw;
+  __shared__ DocMask dmask;
   Lane L;
-  if (!lane_coords<V>(a.nvec, a.rows, a.bands, a.C, L)) return;
+  const bool active = lane_coords<V>(a.nvec, a.rows, a.bands, a.C, L);
   const int32_t row_bytes = a.C * 2;
-  const uint32_t nrec = span_bytes(a.S, a.C, L.base_row);
+  const uint32_t nrec = span_bytes(a.S, a.C, L.base_row);  // wave-uniform
   const rsrc_t rx = make_rsrc(a.x + (int64_t)L.base_row * a.C, nrec);
   const rsrc_t ry = make_rsrc(a.y + (int64_t)L.base_row * a.C, nrec);
+
+  // The halo rows t0-3 .. t0-1 and the first group are requested before the
+  // workgroup resolves its document starts.
+  int32_t r = L.t0 - 3;
+  int32_t off = L.off;
+  Raw halo[3], A[kFwdGroup], B[kFwdGroup];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) halo[q] = VT::zero();
+  off += 3 * row_bytes;
+  if (active) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      if (r + q >= 0) halo[q] = VT::load(rx, off + (q - 3) * row_bytes);
+#pragma unroll
+    for (int g = 0; g < kFwdGroup; ++g) A[g] = VT::load(rx, off + g * row_bytes);
+  }
+
+  build_doc_mask(dmask, a.cu, a.num_docs, a.nvec, a.rows, a.bands);
+  if (!active) return;
 
   float w[4][V], bv[V];
   load_weights<V>(a.w, a.w_bf16, L.vec * V, w);
   if (kBias) load_bias<V>(a.b, a.b_bf16, L.vec * V, bv);
 
-  int32_t r = L.t0 - 3;
-  int32_t off = L.off;
-  DocWalk walk;
-  walk.init(a.cu, a.num_docs, max(r, 0));
-
   // Window of the three previous rows: h1 = x[r-1], h2 = x[r-2], h3 = x[r-3].
   float h1[V], h2[V], h3[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) h1[i] = h2[i] = h3[i] = 0.0f;
-
-  // Halo rows t0-3 .. t0-1 (before the first token nothing is read).
+  const uint32_t hs = doc_starts(dmask, r, 3);
 #pragma unroll
-  for (int q = 0; q < 3; ++q, ++r, off += row_bytes) {
-    typename VT::raw v = VT::zero();
-    if (r >= 0) v = VT::load(rx, off);
-    if (r == walk.next) {
+  for (int q = 0; q < 3; ++q) {
+    if ((hs >> q) & 1u) {
 #pragma unroll
       for (int i = 0; i < V; ++i) h1[i] = h2[i] = 0.0f;
-      walk.advance(r);
     }
 #pragma unroll
     for (int i = 0; i < V; ++i) h3[i] = h2[i], h2[i] = h1[i];
-    unpack<V>(v, h1);
+    unpack<V>(halo[q], h1);
   }
+  r += 3;
 
   // Groups of G rows, two register buffers: the loads of group k+1 are in
   // flight while group k is computed; a group's y rows are stored together
   // after its last row (loads and stores share one wait counter on this
   // architecture, so a store between loads would stall the next wait).
-  typedef typename VT::raw Raw;
   auto load = [&](Raw (&buf)[kFwdGroup], int32_t at) {
 #pragma unroll
     for (int g = 0; g < kFwdGroup; ++g) buf[g] = VT::load(rx, at + g * row_bytes);
   };
-  auto run = [&](Raw (&buf)[kFwdGroup]) {
-    if (walk.next > r + (kFwdGroup - 1)) {
+  auto run = [&](const Raw (&buf)[kFwdGroup]) {
+    // y goes to its own registers: the loaded rows stay read-only.
+    Raw out[kFwdGroup];
+    const uint32_t starts = doc_starts(dmask, r, kFwdGroup);
+    if (starts == 0u) {
       // No document starts in this group.
 #pragma unroll
       for (int g = 0; g < kFwdGroup; ++g) {
         float xc[V];
         unpack<V>(buf[g], xc);
-        buf[g] = fwd_row<kBias, V>(w, bv, h3, h2, h1, xc);
+        out[g] = fwd_row<kBias, V>(w, bv, h3, h2, h1, xc);
 #pragma unroll
         for (int i = 0; i < V; ++i) h3[i] = h2[i], h2[i] = h1[i], h1[i] = xc[i];
       }
     } else {
 #pragma unroll
       for (int g = 0; g < kFwdGroup; ++g) {
-        if (r + g == walk.next) {
+        if ((starts >> g) & 1u) {
 #pragma unroll
           for (int i = 0; i < V; ++i) h1[i] = h2[i] = h3[i] = 0.0f;
-          walk.advance(r + g);
         }
         float xc[V];
         unpack<V>(buf[g], xc);
-        buf[g] = fwd_row<kBias, V>(w, bv, h3, h2, h1, xc);
+        out[g] = fwd_row<kBias, V>(w, bv, h3, h2, h1, xc);
 #pragma unroll
         for (int i = 0; i < V; ++i) h3[i] = h2[i], h2[i] = h1[i], h1[i] = xc[i];
       }
     }
 #pragma unroll
-    for (int g = 0; g < kFwdGroup; ++g) VT::store(ry, off + g * row_bytes, buf[g]);
+    for (int g = 0; g < kFwdGroup; ++g) VT::store(ry, off + g * row_bytes, out[g]);
     r += kFwdGroup;
     off += kFwdGroup * row_bytes;
   };
   // T is a multiple of 2G (host rule).
-  Raw A[kFwdGroup], B[kFwdGroup];
-  load(A, off);
   for (int32_t done = 0; done < a.rows; done += 2 * kFwdGroup) {
     load(B, off + kFwdGroup * row_bytes);
     run(A);
@@ -584,58 +645,73 @@ template <bool kBias, bool kBf16Policy, typename Acc, int V>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kBwdWaves)))
 void bwd_main_kernel(BwdArgs a) {
   typedef Vec<V> VT;
+  typedef typename VT::raw Raw;
   __shared__ float lut_lds[kBf16Policy ? 2 * kLutN : 1];
-  if (kBf16Policy) {
-    // Every thread helps to stage the table before any may leave.
-    for (int i = threadIdx.x; i < 2 * kLutN; i += kBlock) lut_lds[i] = kSiluGradTable.v[i];
-    __syncthreads();
-  }
+  __shared__ DocMask dmask;
   Lane L;
-  if (!lane_coords<V>(a.nvec, a.rows, a.bands, a.C, L)) return;
+  const bool active = lane_coords<V>(a.nvec, a.rows, a.bands, a.C, L);
   const int32_t row_bytes = a.C * 2;
-  const uint32_t nrec = span_bytes(a.S, a.C, L.base_row);
+  const uint32_t nrec = span_bytes(a.S, a.C, L.base_row);  // wave-uniform
   const int64_t base_elt = (int64_t)L.base_row * a.C;
   const rsrc_t rx = make_rsrc(a.x + base_elt, nrec);
   const rsrc_t rdy = make_rsrc(a.dy + base_elt, nrec);
   const rsrc_t rdx = make_rsrc(a.dx + base_elt, nrec);
 
+  // The halo rows t0-3 .. t0-1 (x only) and the first group are requested
+  // before the workgroup stages its tables.
+  int32_t r = L.t0 - 3;
+  int32_t off = L.off;
+  Raw halo[3], xa[kBwdGroup], da[kBwdGroup], xb[kBwdGroup], db[kBwdGroup];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) halo[q] = VT::zero();
+  off += 3 * row_bytes;
+  if (active) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q)
+      if (r + q >= 0) halo[q] = VT::load(rx, off + (q - 3) * row_bytes);
+#pragma unroll
+    for (int g = 0; g < kBwdGroup; ++g) {
+      xa[g] = VT::load(rx, off + g * row_bytes);
+      da[g] = VT::load(rdy, off + g * row_bytes);
+    }
+  }
+
+  if (kBf16Policy) {
+    // Every thread helps to stage the SiLU' table (the mask builder's
+    // barriers make it visible).
+    for (int i = threadIdx.x; i < 2 * kLutN; i += kBlock) lut_lds[i] = kSiluGradTable.v[i];
+  }
+  build_doc_mask(dmask, a.cu, a.num_docs, a.nvec, a.rows, a.bands);
+  if (!active) return;
+
   float w[4][V], bv[V];
   load_weights<V>(a.w, a.w_bf16, L.vec * V, w);
   if (kBias) load_bias<V>(a.b, a.b_bf16, L.vec * V, bv);
-
   Partials<Acc, V> acc;
 #pragma unroll
   for (int k = 0; k < 5; ++k)
 #pragma unroll
     for (int i = 0; i < V; ++i) acc.v[k][i] = (Acc)0;
 
-  int32_t r = L.t0 - 3;
-  int32_t off = L.off;
-  DocWalk walk;
-  walk.init(a.cu, a.num_docs, max(r, 0));
-  uint32_t hist = 0;  // bit 0 = row r-1 starts a document, bit 1 = row r-2
-
   float h1[V], h2[V], h3[V], d1[V], d2[V], d3[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) h1[i] = h2[i] = h3[i] = d1[i] = d2[i] = d3[i] = 0.0f;
-
-  // Halo rows t0-3 .. t0-1: x only.
+  // hist: bit 0 = row r-1 starts a document, bit 1 = row r-2.
+  const uint32_t hs = doc_starts(dmask, r, 3);
+  uint32_t hist = 0;
 #pragma unroll
-  for (int q = 0; q < 3; ++q, ++r, off += row_bytes) {
-    typename VT::raw v = VT::zero();
-    if (r >= 0) v = VT::load(rx, off);
-    uint32_t start = 0;
-    if (r == walk.next) {
+  for (int q = 0; q < 3; ++q) {
+    const uint32_t start = (hs >> q) & 1u;
+    if (start) {
 #pragma unroll
       for (int i = 0; i < V; ++i) h1[i] = h2[i] = 0.0f;
-      walk.advance(r);
-      start = 1;
     }
     hist = ((hist << 1) | start) & 3u;
 #pragma unroll
     for (int i = 0; i < V; ++i) h3[i] = h2[i], h2[i] = h1[i];
-    unpack<V>(v, h1);
+    unpack<V>(halo[q], h1);
   }
+  r += 3;
 
   // Band rows t0 .. t0+T-1 (partials) in groups of G with two register
   // buffers: the loads of group k+1 are in flight while group k is
@@ -644,7 +720,6 @@ void bwd_main_kernel(BwdArgs a) {
   // t0+idx emits dx of row t0+idx-3, so the band's first three rows emit
   // nothing and three look-ahead rows, loaded during the last group,
   // finish the band.
-  typedef typename VT::raw Raw;
   auto load = [&](Raw (&xr)[kBwdGroup], Raw (&dr)[kBwdGroup], int32_t at, int nrows) {
 #pragma unroll
     for (int g = 0; g < kBwdGroup; ++g) {
@@ -654,9 +729,14 @@ void bwd_main_kernel(BwdArgs a) {
       }
     }
   };
-  auto run = [&](Raw (&xr)[kBwdGroup], Raw (&dr)[kBwdGroup], int32_t done, int nrows,
+  auto run = [&](const Raw (&xr)[kBwdGroup], const Raw (&dr)[kBwdGroup], int32_t done, int nrows,
                  bool accumulate) {
-    if (hist == 0 && walk.next > r + (nrows - 1)) {
+    // dx goes to its own registers: the loaded rows stay read-only.
+    Raw dxr[kBwdGroup];
+#pragma unroll
+    for (int g = 0; g < kBwdGroup; ++g) dxr[g] = VT::zero();
+    const uint32_t starts = doc_starts(dmask, r, nrows);
+    if (hist == 0u && starts == 0u) {
       // No document starts in rows r-2 .. r+nrows-1: no resets, no masks.
 #pragma unroll
       for (int g = 0; g < kBwdGroup; ++g) {
@@ -665,18 +745,16 @@ void bwd_main_kernel(BwdArgs a) {
         unpack<V>(xr[g], xc);
         bwd_row<kBias, kBf16Policy, false, Acc, V>(w, bv, lut_lds, xc, dr[g], h1, h2, h3, d1, d2,
                                                    d3, acc, accumulate, done + g >= 3, 0u,
-                                                   xr[g]);
+                                                   dxr[g]);
       }
     } else {
 #pragma unroll
       for (int g = 0; g < kBwdGroup; ++g) {
         if (g >= nrows) break;
-        uint32_t start = 0;
-        if (r + g == walk.next) {
+        const uint32_t start = (starts >> g) & 1u;
+        if (start) {
 #pragma unroll
           for (int i = 0; i < V; ++i) h1[i] = h2[i] = h3[i] = 0.0f;
-          walk.advance(r + g);
-          start = 1;
         }
         const uint32_t h3bits = (hist << 1) | start;
         hist = h3bits & 3u;
@@ -684,19 +762,17 @@ void bwd_main_kernel(BwdArgs a) {
         unpack<V>(xr[g], xc);
         bwd_row<kBias, kBf16Policy, true, Acc, V>(w, bv, lut_lds, xc, dr[g], h1, h2, h3, d1, d2,
                                                   d3, acc, accumulate, done + g >= 3, h3bits,
-                                                  xr[g]);
+                                                  dxr[g]);
       }
     }
-    // xr[g] now holds the packed dx of row r+g-3.
+    // dxr[g] holds the packed dx of row r+g-3.
 #pragma unroll
     for (int g = 0; g < kBwdGroup; ++g)
-      if (g < nrows && done + g >= 3) VT::store(rdx, off + (g - 3) * row_bytes, xr[g]);
+      if (g < nrows && done + g >= 3) VT::store(rdx, off + (g - 3) * row_bytes, dxr[g]);
     r += nrows;
     off += nrows * row_bytes;
   };
   // T is a multiple of 2G (host rule).
-  Raw xa[kBwdGroup], da[kBwdGroup], xb[kBwdGroup], db[kBwdGroup];
-  load(xa, da, off, kBwdGroup);
   for (int32_t done = 0; done < a.rows; done += 2 * kBwdGroup) {
     load(xb, db, off + kBwdGroup * row_bytes, kBwdGroup);
     run(xa, da, done, kBwdGroup, true);
@@ -790,13 +866,14 @@ hipError_t launch_bwd_main_v(const Plan& plan, const BwdArgs& a, bool has_bias, 
 // ============================================================ launchers ==
 
 hipError_t launch_fwd(const Plan& plan, const FwdArgs& a, bool has_bias, hipStream_t s) {
-  return plan.vec == 8 ? launch_fwd_v<8>(plan, a, has_bias, s) : launch_fwd_v<4>(plan, a, has_bias, s);
+  if (plan.vec != kFwdVec) return hipErrorInvalidValue;
+  return launch_fwd_v<kFwdVec>(plan, a, has_bias, s);
 }
 
 hipError_t launch_bwd_main(const Plan& plan, const BwdArgs& a, bool has_bias, bool fp32_policy,
                            hipStream_t s) {
-  return plan.vec == 8 ? launch_bwd_main_v<8>(plan, a, has_bias, fp32_policy, s)
-                       : launch_bwd_main_v<4>(plan, a, has_bias, fp32_policy, s);
+  if (plan.vec != kBwdVec) return hipErrorInvalidValue;
+  return launch_bwd_main_v<kBwdVec>(plan, a, has_bias, fp32_policy, s);
 }
 
 hipError_t launch_bwd_reduce(const Plan& plan, const ReduceArgs& a, bool fp64, hipStream_t s) {
