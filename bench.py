@@ -7,8 +7,16 @@ HBM, timed with HIP events on the stream the library launches on.
 Prints one JSON line.  `value` is the step's algorithmic HBM traffic
 (forward 4 B + backward 6 B per token-channel, plus parameters) divided by
 the step time, in GB/s; per-direction GB/s, Mtokens/s and fractions of the
-8 TB/s MI355X HBM peak are alongside.  `cpu_baseline` times the FP64 CPU
-oracle on a bounded sample of the same workload on this host.
+8 TB/s MI355X HBM peak are alongside.  `roofline` prices one conv1d_bwd call
+(the main kernel and the small fixed-order reduce it enqueues) and
+`roofline_fwd` the forward kernel: algorithmic bytes over the mean
+event-timed launch, and, when profiles/headline_counters.md was taken on
+these same kernel sources, the HBM traffic the rocprofv3 counters saw per
+launch at the same duration.  `cpu_baseline` times the FP64 CPU oracle on a
+bounded sample of the same workload on this host.
+
+`--copy-calibration` instead times a plain device copy of one [S, C] BF16
+tensor: the reference kernel of known size that scales the byte counters.
 """
 from __future__ import annotations
 
@@ -27,6 +35,12 @@ METRIC = "fwd/bwd HBM GB/s + Mtokens/s, S=64K C=4096 packed; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = "headline"
 CPU_SAMPLE_CHANNELS = 4096
+# HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
+# WRITE_SIZE, scaled by a plain copy's reading) for the kernels as built from
+# the sources whose digest the file records; ignored once the sources differ.
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "headline_counters.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "varlen_depthwise_causal_amd", "csrc", f)
+                  for f in ("vdc_kernels.hip", "vdc_internal.h", "vdc_api.cpp")]
 
 
 def algorithmic_bytes(wl, direction):
@@ -39,6 +53,57 @@ def algorithmic_bytes(wl, direction):
         return 4 * S * C + pw + pb + cu            # read x, write y
     # read x and dy, write dx; write dweight and dbias (FP32 here)
     return 6 * S * C + pw + pb + cu + C * 4 * 4 + (0 if wl.b is None else C * 4)
+
+
+def sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(policy):
+    """{kernel: bytes per launch} from the committed counter summary, or None
+    when it is missing, was taken on other sources, or for another policy."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return None
+    for line in lines:
+        if line.startswith("traffic-json: "):
+            rec = json.loads(line[len("traffic-json: "):])
+            if rec.get("sources") == sources_digest() and rec.get("policy") == policy:
+                return rec
+    return None
+
+
+def copy_calibration(steps, warmup):
+    """Time a plain device copy of one [S, C] BF16 tensor (the reference for
+    scaling the HBM byte counters and a practical bandwidth ceiling)."""
+    import torch
+    from varlen_depthwise_causal_amd import workloads as W
+    spec = W.SPECS[WORKLOAD]
+    dev = torch.device("cuda:0")
+    x = torch.empty((spec.S, spec.C), dtype=torch.bfloat16, device=dev).fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(warmup):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        y.copy_(x)
+        e[1].record()
+    torch.cuda.synchronize()
+    ms = statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
+    nbytes = 2 * x.numel() * x.element_size()
+    print(json.dumps({"copy_calibration": {"S": spec.S, "C": spec.C, "bytes_read": nbytes // 2,
+                                           "bytes_written": nbytes // 2, "ms": round(ms, 4),
+                                           "GB_s": round(nbytes / (ms * 1e-3) / 1e9, 2),
+                                           "steps": steps}}), flush=True)
 
 
 def gpu_leg(wl, policy, steps, warmup):
@@ -120,15 +185,34 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--policy", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="time a plain copy of one [S, C] BF16 tensor instead")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this path runs on one GPU only (no multi-GPU sharding is built); "
               "run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.steps, args.warmup)
+        return
 
     from varlen_depthwise_causal_amd import workloads as W
     wl = W.make(WORKLOAD, workers=16)
     g = gpu_leg(wl, args.policy, args.steps, args.warmup)
+
+    traffic = counted_traffic(args.policy)
+
+    def roofline(kernel, alg_bytes, ms, counted, names):
+        achieved = alg_bytes / (ms * 1e-3) / 1e9
+        out = {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 2),
+               "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+               "traffic": None, "algorithmic_bytes": alg_bytes, "launch_ms": round(ms, 4)}
+        if counted is not None:
+            nbytes = sum(counted["bytes_per_launch"][n] for n in names)
+            out["traffic"] = round(nbytes / (ms * 1e-3) / 1e9, 2)
+            out["traffic_bytes"] = nbytes
+            out["traffic_over_algorithmic"] = round(nbytes / alg_bytes, 4)
+        return out
 
     fwd_ms = statistics.mean(g["fwd_ms"])
     bwd_ms = statistics.mean(g["bwd_ms"])
@@ -167,12 +251,9 @@ def main():
                 "mtokens_per_s": round(wl.S / (bwd_ms * 1e-3) / 1e6, 3),
                 "algorithmic_bytes": bb, "plan": g["plan_bwd"],
                 "partial_bytes": 2 * g["plan_bwd"]["bands"] * 5 * wl.C * g["plan_bwd"]["acc_bytes"]},
-        "roofline": {"kernel": "conv1d_bwd: bwd_main_kernel + bwd_reduce_kernel (one call)",
-                     "bound": "hbm", "achieved": round(bwd_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(bwd_gbs / HBM_PEAK_GBS, 4), "traffic": None},
-        "roofline_fwd": {"kernel": "fwd_kernel", "bound": "hbm", "achieved": round(fwd_gbs, 2),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(fwd_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "roofline": roofline("conv1d_bwd (bwd_main_kernel then bwd_reduce_kernel, one call)",
+                             bb, bwd_ms, traffic, ("bwd_main_kernel", "bwd_reduce_kernel")),
+        "roofline_fwd": roofline("fwd_kernel", fb, fwd_ms, traffic, ("fwd_kernel",)),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_leg(wl, args.policy)
