@@ -43,6 +43,17 @@ def bf16_bits(t):
     return t.detach().to("cpu").view(torch.int16).numpy().view(np.uint16)
 
 
+def small_case(seed, S, C, lengths, w_dtype, b_dtype, sat):
+    """A seeded case of the given shape; lengths "randint" draws U{0..25}
+    document lengths (the Stress recipe) with a remainder document."""
+    if lengths == "randint":
+        rng = np.random.default_rng(seed)
+        lengths = list(rng.integers(0, 26, size=S // 14))
+        lengths.append(S - sum(lengths))
+    return W.random_case(seed, S, C, lengths, w_dtype=w_dtype, b_dtype=b_dtype,
+                         w_scale=1.0 if sat else 0.5, b_scale=0.5 if sat else 0.1, sat=sat)
+
+
 @functools.lru_cache(maxsize=4)
 def named(name):
     return W.make(name, workers=16)

@@ -44,13 +44,7 @@ SMALL = [
 ]
 
 
-def _small(seed, S, C, lengths, w_dtype, b_dtype, sat):
-    if lengths == "randint":
-        rng = np.random.default_rng(seed)
-        lengths = list(rng.integers(0, 26, size=S // 14))
-        lengths.append(S - sum(lengths))
-    return W.random_case(seed, S, C, lengths, w_dtype=w_dtype, b_dtype=b_dtype,
-                         w_scale=1.0 if sat else 0.5, b_scale=0.5 if sat else 0.1, sat=sat)
+_small = G.small_case
 
 
 @pytest.mark.parametrize("policy", ["bf16", "fp32"])

@@ -282,10 +282,14 @@ __device__ __forceinline__ float sigmoid_scaled64(float z) {
                                __builtin_amdgcn_exp2f(__builtin_fmaf(z, -kLog2e, -64.0f)));
 }
 
-// SiLU'(z) = s * (1 + z * (1 - s)), evaluated as fma(z - z*s, s, s).
+// SiLU'(z) = s * (1 + z * (1 - s)) with s = 1 / (1 + e), e = exp(-z).
+// 1 - s is formed as e * s, which keeps its relative accuracy where s is
+// close to 1; forming it as 1 - s (or z - z*s) would leave an absolute
+// error of about z * 2^-24 in SiLU' for large positive z.
 __device__ __forceinline__ float silu_grad_fast(float z) {
-  float s = sigmoid_fast(z);
-  float t = __builtin_fmaf(-z, s, z);
+  const float e = __builtin_amdgcn_exp2f(-z * kLog2e);
+  const float s = __builtin_amdgcn_rcpf(1.0f + e);
+  const float t = z * (e * s);
   return __builtin_fmaf(t, s, s);
 }
 
