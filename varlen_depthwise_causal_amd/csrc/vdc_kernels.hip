@@ -555,13 +555,39 @@ void fwd_kernel(FwdArgs a) {
 
 // ================================================ backward main kernel ==
 
-__device__ __forceinline__ float fma_acc(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
-__device__ __forceinline__ double fma_acc(double a, double b, double c) { return __builtin_fma(a, b, c); }
-
+// A lane's gradient partials: taps k = 0..3, then the bias term.  Under the
+// "bf16" policy (Acc = float) every row is added straight into the binary32
+// totals `v`.  Under "fp32" (Acc = double) the rows of one row group (G
+// rows) are summed in binary32 in `run`, and each group's sum is added into
+// the binary64 totals: a run of G products rounds within a few units in the
+// last place of its own magnitude, and no error grows with the band length,
+// at an eighth of the binary64 operations of a per-row binary64 sum.
 template <typename Acc, int V>
 struct Partials {
-  Acc v[5][V];  // taps k = 0..3, then the bias term
+  Acc v[5][V];
+  float run[5][V];
 };
+
+// Where a row's contributions go: the binary32 run under "fp32", the totals
+// themselves under "bf16".
+template <typename Acc, int V>
+__device__ __forceinline__ float (&row_sums(Partials<Acc, V>& acc))[5][V] {
+  if constexpr (sizeof(Acc) == 8) return acc.run;
+  else return acc.v;
+}
+
+template <typename Acc, int V>
+__device__ __forceinline__ void fold_partials(Partials<Acc, V>& acc) {
+  if constexpr (sizeof(Acc) == 8) {
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        acc.v[k][i] += (Acc)acc.run[k][i];
+        acc.run[k][i] = 0.0f;
+      }
+  }
+}
 
 // dpre = dy * SiLU'(z) for the lane's V channels of one row.
 template <bool kBf16Policy, int V>
@@ -609,17 +635,15 @@ __device__ __forceinline__ void bwd_row(const float (&w)[4][V], const float (&bv
   for (int i = 0; i < V; ++i) p[i] = preact<kBias, V>(w, bv, i, h3[i], h2[i], h1[i], xc[i]);
   dpre_row<kBf16Policy, V>(p, dyv, lut, dp);
   if (accumulate) {
-    // acc_k += dpre * x[v-3+k] as one fused multiply-add (the product of
-    // two binary32 values is exact in binary64, so under FP64 accumulation
-    // only the sum rounds); acc_4 += dpre.
+    // acc_k += dpre * x[v-3+k] as one fused multiply-add; acc_4 += dpre.
+    float(&dst)[5][V] = row_sums(acc);
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-      const Acc g = (Acc)dp[i];
-      acc.v[0][i] = fma_acc(g, (Acc)h3[i], acc.v[0][i]);
-      acc.v[1][i] = fma_acc(g, (Acc)h2[i], acc.v[1][i]);
-      acc.v[2][i] = fma_acc(g, (Acc)h1[i], acc.v[2][i]);
-      acc.v[3][i] = fma_acc(g, (Acc)xc[i], acc.v[3][i]);
-      acc.v[4][i] += g;
+      dst[0][i] = __builtin_fmaf(dp[i], h3[i], dst[0][i]);
+      dst[1][i] = __builtin_fmaf(dp[i], h2[i], dst[1][i]);
+      dst[2][i] = __builtin_fmaf(dp[i], h1[i], dst[2][i]);
+      dst[3][i] = __builtin_fmaf(dp[i], xc[i], dst[3][i]);
+      dst[4][i] += dp[i];
     }
   }
   if (emit) {
@@ -695,7 +719,7 @@ void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < 5; ++k)
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc.v[k][i] = (Acc)0;
+    for (int i = 0; i < V; ++i) acc.v[k][i] = (Acc)0, acc.run[k][i] = 0.0f;
 
   float h1[V], h2[V], h3[V], d1[V], d2[V], d3[V];
 #pragma unroll
@@ -773,6 +797,7 @@ void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int g = 0; g < kBwdGroup; ++g)
       if (g < nrows && done + g >= 3) VT::store(rdx, off + (g - 3) * row_bytes, dxr[g]);
+    if (accumulate) fold_partials(acc);
     r += nrows;
     off += nrows * row_bytes;
   };
