@@ -99,9 +99,10 @@ enum vdc_status {
  * serves every route of the direction.  VDC_FWD: the forward keeps no
  * counters and needs no workspace, so the answer is 0 (conv1d_fwd accepts
  * workspace = NULL).  VDC_BWD: room for the per-band FP32 / FP64 partial
- * rows of dweight and dbias for every policy, at this (S, C); the backward
- * writes every byte it later reads, so the buffer needs no zeroing
- * ([B] Parameters workspace).
+ * rows of dweight and dbias for every policy, at this (S, C), plus the
+ * FP64 sums of the reduce's first stage when there are more than 2048
+ * partial rows; the backward writes every byte it later reads, so the
+ * buffer needs no zeroing ([B] Parameters workspace).
  *
  * direction: VDC_FWD or VDC_BWD.  S >= 0 tokens, C > 0 channels (a multiple
  * of 8).  Returns 0 for invalid arguments (and for every valid forward).
@@ -147,10 +148,13 @@ int conv1d_fwd(const void *x, const void *weight, int w_dtype,
  *            contents irrelevant; must not overlap any other argument.
  *
  * Two launches are enqueued in stream order: the main kernel writes dx and
- * one partial row of dweight / dbias per band of tokens into the workspace,
- * and the reduce kernel sums the rows in a fixed order (FP32 under
- * VDC_SILU_GRAD_BF16, FP64 under VDC_SILU_GRAD_FP32) and rounds once to the
- * output dtype ([B] Description).  S == 0 launches neither kernel: dweight
+ * one partial row of dweight / dbias per band of tokens into the workspace
+ * (FP32 under VDC_SILU_GRAD_BF16, FP64 under VDC_SILU_GRAD_FP32), and the
+ * reduce kernel sums the rows in FP64 in a fixed order and rounds once to
+ * the output dtype ([B] Description).  With more than 2048 partial rows
+ * (long sequences of few channels) the reduce takes two launches: sums of
+ * 2048-row ranges, then their sum, in an order that again depends on
+ * (S, C) only.  S == 0 launches neither kernel: dweight
  * (and dbias) are set to zero with hipMemsetAsync, or, if the stream is
  * being captured into a graph, with a small fill kernel ([B] Returns).
  * Returns a vdc_status.
@@ -174,7 +178,8 @@ const char *conv1d_status_string(int status);
  * backward), lanes (bands * C / channels per lane), main-kernel workgroups,
  * threads per workgroup, partial element bytes (0 forward, 4 or 8
  * backward), reduce-kernel workgroups, reduce chunks, channels per lane,
- * 0 }.  Returns a vdc_status.
+ * first-stage reduce row ranges (0 when the reduce is one launch) }.
+ * Returns a vdc_status.
  */
 int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int64_t out[10]);
 

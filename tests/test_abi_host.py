@@ -167,6 +167,12 @@ def test_plans_depend_on_shape_only(lib):
             block_rows = (-(-threads // (C // vec)) + 1) * rows + 6
             assert block_rows < 32 * 1023
             assert bands * rows >= S and (bands - 1) * rows < max(S, 1)
+            stage1 = a[9]
+            if d == BWD:
+                assert stage1 == (0 if bands <= 2048 else -(-bands // 2048))
+                assert lib.workspace_bytes(BWD, S, C) == (bands + stage1) * 5 * C * 8
+            else:
+                assert stage1 == 0
 
 
 def test_status_strings(lib):

@@ -111,7 +111,7 @@ def conv1d_plan(direction: str, S: int, C: int, policy: str = "bf16") -> dict:
     if rc:
         raise VdcError(rc, "conv1d_plan")
     keys = ("rows", "bands", "lanes", "blocks", "threads", "acc_bytes", "red_blocks", "red_chunks",
-            "vec")
+            "vec", "red_stage1")
     return dict(zip(keys, (int(v) for v in out)))
 
 

@@ -8,6 +8,7 @@
 #include "vdc.h"
 
 #include <algorithm>
+#include <climits>
 #include <atomic>
 #include <stdint.h>
 
@@ -94,9 +95,14 @@ Plan make_plan(int dir, int64_t S, int64_t C, int policy) {
   p.blocks = (int32_t)ceil_div(p.lanes, kBlock);
   p.acc_bytes = dir == VDC_FWD ? 0 : (policy == VDC_SILU_GRAD_FP32 ? 8 : 4);
   p.red_blocks = dir == VDC_FWD ? 0 : (int32_t)ceil_div(5 * C, kRedOut);
-  p.red_rows = dir == VDC_FWD ? 0 : (int32_t)ceil_div(p.bands, kRedChunks);
+  p.red_stage1 = (dir == VDC_FWD || p.bands <= kRedBlockRows)
+                     ? 0
+                     : (int32_t)ceil_div(p.bands, kRedBlockRows);
   return p;
 }
+
+// Lane and workgroup indices are 32-bit in the kernels.
+bool plan_fits(const Plan& p) { return p.lanes <= (int64_t)INT32_MAX - kBlock; }
 
 int check_sizes(int64_t S, int64_t C, int64_t num_docs) {
   if (C <= 0 || C % 8 != 0 || C > kMaxC) return VDC_EINVAL;
@@ -119,9 +125,11 @@ extern "C" size_t workspace_bytes(int direction, int64_t S, int64_t C) {
   if (direction != VDC_FWD && direction != VDC_BWD) return 0;
   if (check_sizes(S, C, S > 0 ? 1 : 0) != VDC_OK) return 0;
   if (direction == VDC_FWD || S == 0) return 0;
-  // Largest partial element over the policies (FP64 under the fp32 policy).
+  // Largest partial element over the policies (FP64 under the fp32 policy),
+  // then the binary64 sums of the reduce's first stage when it has one.
   const Plan p = make_plan(VDC_BWD, S, C, VDC_SILU_GRAD_FP32);
-  return (size_t)p.bands * 5 * (size_t)C * 8;
+  if (!plan_fits(p)) return 0;
+  return ((size_t)p.bands + (size_t)p.red_stage1) * 5 * (size_t)C * 8;
 }
 
 extern "C" int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int64_t out[10]) {
@@ -132,6 +140,7 @@ extern "C" int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int6
   int rc = check_sizes(S, C, S > 0 ? 1 : 0);
   if (rc) return rc;
   const Plan p = make_plan(direction, S, C, policy);
+  if (!plan_fits(p)) return VDC_EINVAL;
   out[0] = p.rows;
   out[1] = p.bands;
   out[2] = p.lanes;
@@ -141,7 +150,7 @@ extern "C" int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int6
   out[6] = p.red_blocks;
   out[7] = kRedChunks;
   out[8] = p.vec;
-  out[9] = 0;
+  out[9] = p.red_stage1;
   return VDC_OK;
 }
 
@@ -166,6 +175,7 @@ extern "C" int conv1d_fwd(const void* x, const void* weight, int w_dtype, const 
   if (overlaps(y, act, cu_seqlens, (size_t)(num_docs + 1) * 4)) return VDC_EINVAL;
 
   const Plan plan = make_plan(VDC_FWD, S, C, 0);
+  if (!plan_fits(plan)) return VDC_EINVAL;
   FwdArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.y = static_cast<uint16_t*>(y);
@@ -222,7 +232,6 @@ extern "C" int conv1d_bwd(const void* x, const void* weight, int w_dtype, const 
     r.db = dbias;
     r.P = 0;
     r.C = (int32_t)C;
-    r.rows_per_chunk = 0;
     r.dw_bf16 = dw_dtype == VDC_BF16;
     r.db_bf16 = db_dtype == VDC_BF16;
     g_launches.fetch_add(1, std::memory_order_relaxed);
@@ -254,6 +263,7 @@ extern "C" int conv1d_bwd(const void* x, const void* weight, int w_dtype, const 
 
   const bool fp32_policy = policy == VDC_SILU_GRAD_FP32;
   const Plan plan = make_plan(VDC_BWD, S, C, policy);
+  if (!plan_fits(plan)) return VDC_EINVAL;
   BwdArgs a{};
   a.x = static_cast<const uint16_t*>(x);
   a.dy = static_cast<const uint16_t*>(dy);
@@ -279,11 +289,21 @@ extern "C" int conv1d_bwd(const void* x, const void* weight, int w_dtype, const 
   r.db = dbias;
   r.P = plan.bands;
   r.C = (int32_t)C;
-  r.rows_per_chunk = plan.red_rows;
   r.dw_bf16 = dw_dtype == VDC_BF16;
   r.db_bf16 = db_dtype == VDC_BF16;
+  bool part_f64 = fp32_policy;
+  if (plan.red_stage1 > 0) {
+    // Many partial rows: sums of kRedBlockRows-row ranges first, into the
+    // workspace after the largest partial-row area, then one pass over them.
+    r.inter = static_cast<char*>(workspace) + (size_t)plan.bands * 5 * (size_t)C * 8;
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    if (launch_bwd_reduce_rows(plan, r, part_f64, stream) != hipSuccess) return VDC_EHIP;
+    r.part = r.inter;
+    r.P = plan.red_stage1;
+    part_f64 = true;
+  }
   g_launches.fetch_add(1, std::memory_order_relaxed);
-  return launch_bwd_reduce(plan, r, fp32_policy, stream) == hipSuccess ? VDC_OK : VDC_EHIP;
+  return launch_bwd_reduce(plan, r, part_f64, stream) == hipSuccess ? VDC_OK : VDC_EHIP;
 }
 
 extern "C" const char* conv1d_status_string(int status) {

@@ -47,6 +47,10 @@ constexpr int kDocMaskWords = 1024;
 
 constexpr int kRedOut = 64;
 constexpr int kRedChunks = 8;
+// Partial rows one first-stage reduce workgroup sums.  With more rows than
+// this the reduce runs in two stages: workgroups of kRedBlockRows rows
+// each, then one pass over their sums; with fewer, one pass.
+constexpr int kRedBlockRows = 2048;
 
 // Everything a launch needs, decided on the host from (direction, S, C,
 // policy) alone - never from tensor contents.
@@ -57,8 +61,8 @@ struct Plan {
   int64_t lanes;       // bands * C / V
   int32_t blocks;      // main-kernel workgroups
   int32_t acc_bytes;   // backward partial element: 4 (FP32) or 8 (FP64)
-  int32_t red_blocks;  // reduce workgroups
-  int32_t red_rows;    // partial rows per reduce chunk
+  int32_t red_blocks;  // reduce workgroups per row range (kRedOut outputs each)
+  int32_t red_stage1;  // first-stage row ranges (0: the reduce is one pass)
 };
 
 struct FwdArgs {
@@ -96,12 +100,12 @@ struct BwdArgs {
 };
 
 struct ReduceArgs {
-  const void* part;    // [P][5][C]
+  const void* part;    // [P][5][C] rows to sum
+  void* inter;         // stage 1 output: [ceil(P / kRedBlockRows)][5][C] binary64
   void* dw;            // [C][4]
   void* db;            // [C] or null
   int32_t P;
   int32_t C;
-  int32_t rows_per_chunk;
   int32_t dw_bf16;
   int32_t db_bf16;
 };
@@ -110,6 +114,9 @@ struct ReduceArgs {
 hipError_t launch_fwd(const Plan& plan, const FwdArgs& a, bool has_bias, hipStream_t s);
 hipError_t launch_bwd_main(const Plan& plan, const BwdArgs& a, bool has_bias, bool fp32_policy,
                            hipStream_t s);
-hipError_t launch_bwd_reduce(const Plan& plan, const ReduceArgs& a, bool fp64, hipStream_t s);
+hipError_t launch_bwd_reduce(const Plan& plan, const ReduceArgs& a, bool part_f64, hipStream_t s);
+// First stage of a two-stage reduce: part rows -> inter (binary64).
+hipError_t launch_bwd_reduce_rows(const Plan& plan, const ReduceArgs& a, bool part_f64,
+                                  hipStream_t s);
 
 }  // namespace vdc

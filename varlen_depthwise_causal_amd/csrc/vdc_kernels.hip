@@ -230,16 +230,20 @@ struct DocMask {
 };
 
 // Every thread of the workgroup must call this (two barriers).  The rows
-// touched are the workgroup's bands plus three halo rows on each side.
+// touched are the workgroup's bands plus three halo rows on each side; the
+// last band's rows may run past S (and past 2^31 - 1), where no start
+// matters, so only starts below S are marked.
 __device__ __forceinline__ void build_doc_mask(DocMask& m, const int32_t* cu, int32_t num_docs,
-                                               int32_t nvec, int32_t rows, int32_t bands) {
+                                               int32_t S, int32_t nvec, int32_t rows,
+                                               int32_t bands) {
   const int32_t g0 = (int32_t)blockIdx.x * kBlock;
   const int32_t first_band = g0 / nvec;
   const int32_t last_band = min((g0 + kBlock - 1) / nvec, bands - 1);
   const int32_t row_lo = first_band * rows - 3;
-  const int32_t row_hi = (last_band + 1) * rows + 3;
+  const int64_t row_end = (int64_t)(last_band + 1) * rows + 3;
   // At most kDocMaskWords + 1 words by the host's choice of rows.
-  const int32_t nwords = ((row_hi - row_lo) >> 5) + 2;
+  const int32_t nwords = (int32_t)((row_end - row_lo) >> 5) + 2;
+  const int32_t row_hi = (int32_t)min(row_end, (int64_t)S);
   for (int32_t i = threadIdx.x; i < nwords; i += kBlock) m.bits[i] = 0u;
   if (threadIdx.x < 64) {
     const int32_t lo = wave_lower_bound(cu, num_docs + 1, max(row_lo, 0));
@@ -260,12 +264,11 @@ __device__ __forceinline__ void build_doc_mask(DocMask& m, const int32_t* cu, in
   __syncthreads();
 }
 
-// Bit g set: row r+g starts a document (1 <= n <= 32, row_lo <= r and
-// r + n <= row_hi of the workgroup).
-__device__ __forceinline__ uint32_t doc_starts(const DocMask& m, int32_t r, int n) {
-  const int32_t b = r - m.row_lo;
+// Bit g set: row row_lo + j + g starts a document, for a row index j
+// relative to the workgroup's first row (1 <= n <= 32).
+__device__ __forceinline__ uint32_t doc_starts(const DocMask& m, int32_t j, int n) {
   const uint32_t bits =
-      __builtin_amdgcn_alignbit(m.bits[(b >> 5) + 1], m.bits[b >> 5], (uint32_t)b & 31u);
+      __builtin_amdgcn_alignbit(m.bits[(j >> 5) + 1], m.bits[j >> 5], (uint32_t)j & 31u);
   return n >= 32 ? bits : bits & ((1u << n) - 1u);
 }
 
@@ -465,7 +468,6 @@ void fwd_kernel(FwdArgs a) {
 
   // The halo rows t0-3 .. t0-1 and the first group are requested before the
   // workgroup resolves its document starts.
-  int32_t r = L.t0 - 3;
   int32_t off = L.off;
   Raw halo[3], A[kFwdGroup], B[kFwdGroup];
 #pragma unroll
@@ -474,12 +476,12 @@ void fwd_kernel(FwdArgs a) {
   if (active) {
 #pragma unroll
     for (int q = 0; q < 3; ++q)
-      if (r + q >= 0) halo[q] = VT::load(rx, off + (q - 3) * row_bytes);
+      if (L.t0 - 3 + q >= 0) halo[q] = VT::load(rx, off + (q - 3) * row_bytes);
 #pragma unroll
     for (int g = 0; g < kFwdGroup; ++g) A[g] = VT::load(rx, off + g * row_bytes);
   }
 
-  build_doc_mask(dmask, a.cu, a.num_docs, a.nvec, a.rows, a.bands);
+  build_doc_mask(dmask, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
   if (!active) return;
 
   float w[4][V], bv[V];
@@ -490,6 +492,8 @@ void fwd_kernel(FwdArgs a) {
   float h1[V], h2[V], h3[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) h1[i] = h2[i] = h3[i] = 0.0f;
+  // Row index relative to the workgroup's first row (no overflow near 2^31).
+  int32_t r = L.t0 - 3 - dmask.row_lo;
   const uint32_t hs = doc_starts(dmask, r, 3);
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
@@ -555,38 +559,30 @@ void fwd_kernel(FwdArgs a) {
 
 // ================================================ backward main kernel ==
 
-// A lane's gradient partials: taps k = 0..3, then the bias term.  Under the
-// "bf16" policy (Acc = float) every row is added straight into the binary32
-// totals `v`.  Under "fp32" (Acc = double) the rows of one row group (G
-// rows) are summed in binary32 in `run`, and each group's sum is added into
-// the binary64 totals: a run of G products rounds within a few units in the
-// last place of its own magnitude, and no error grows with the band length,
-// at an eighth of the binary64 operations of a per-row binary64 sum.
+// A lane's gradient partials: taps k = 0..3, then the bias term.  The rows
+// of one row group (G rows) are summed in binary32 in `run`, and each
+// group's sum is added into the band totals `v`: binary64 under the "fp32"
+// policy (Acc = double), binary32 under "bf16" (Acc = float).  A run of G
+// products rounds within a few units in the last place of its own
+// magnitude; the totals then take T/G additions instead of T, which bounds
+// the binary32 error of a band by about (G + T/G) units in the last place
+// of its sum of magnitudes instead of T.  Under "fp32" this costs an eighth
+// of the binary64 operations of a per-row binary64 sum.
 template <typename Acc, int V>
 struct Partials {
   Acc v[5][V];
   float run[5][V];
 };
 
-// Where a row's contributions go: the binary32 run under "fp32", the totals
-// themselves under "bf16".
-template <typename Acc, int V>
-__device__ __forceinline__ float (&row_sums(Partials<Acc, V>& acc))[5][V] {
-  if constexpr (sizeof(Acc) == 8) return acc.run;
-  else return acc.v;
-}
-
 template <typename Acc, int V>
 __device__ __forceinline__ void fold_partials(Partials<Acc, V>& acc) {
-  if constexpr (sizeof(Acc) == 8) {
 #pragma unroll
-    for (int k = 0; k < 5; ++k)
+  for (int k = 0; k < 5; ++k)
 #pragma unroll
-      for (int i = 0; i < V; ++i) {
-        acc.v[k][i] += (Acc)acc.run[k][i];
-        acc.run[k][i] = 0.0f;
-      }
-  }
+    for (int i = 0; i < V; ++i) {
+      acc.v[k][i] += (Acc)acc.run[k][i];
+      acc.run[k][i] = 0.0f;
+    }
 }
 
 // dpre = dy * SiLU'(z) for the lane's V channels of one row.
@@ -636,7 +632,7 @@ __device__ __forceinline__ void bwd_row(const float (&w)[4][V], const float (&bv
   dpre_row<kBf16Policy, V>(p, dyv, lut, dp);
   if (accumulate) {
     // acc_k += dpre * x[v-3+k] as one fused multiply-add; acc_4 += dpre.
-    float(&dst)[5][V] = row_sums(acc);
+    float(&dst)[5][V] = acc.run;
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       dst[0][i] = __builtin_fmaf(dp[i], h3[i], dst[0][i]);
@@ -687,7 +683,6 @@ void bwd_main_kernel(BwdArgs a) {
 
   // The halo rows t0-3 .. t0-1 (x only) and the first group are requested
   // before the workgroup stages its tables.
-  int32_t r = L.t0 - 3;
   int32_t off = L.off;
   Raw halo[3], xa[kBwdGroup], da[kBwdGroup], xb[kBwdGroup], db[kBwdGroup];
 #pragma unroll
@@ -696,7 +691,7 @@ void bwd_main_kernel(BwdArgs a) {
   if (active) {
 #pragma unroll
     for (int q = 0; q < 3; ++q)
-      if (r + q >= 0) halo[q] = VT::load(rx, off + (q - 3) * row_bytes);
+      if (L.t0 - 3 + q >= 0) halo[q] = VT::load(rx, off + (q - 3) * row_bytes);
 #pragma unroll
     for (int g = 0; g < kBwdGroup; ++g) {
       xa[g] = VT::load(rx, off + g * row_bytes);
@@ -709,7 +704,7 @@ void bwd_main_kernel(BwdArgs a) {
     // barriers make it visible).
     for (int i = threadIdx.x; i < 2 * kLutN; i += kBlock) lut_lds[i] = kSiluGradTable.v[i];
   }
-  build_doc_mask(dmask, a.cu, a.num_docs, a.nvec, a.rows, a.bands);
+  build_doc_mask(dmask, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
   if (!active) return;
 
   float w[4][V], bv[V];
@@ -725,6 +720,8 @@ void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < V; ++i) h1[i] = h2[i] = h3[i] = d1[i] = d2[i] = d3[i] = 0.0f;
   // hist: bit 0 = row r-1 starts a document, bit 1 = row r-2.
+  // Row index relative to the workgroup's first row (no overflow near 2^31).
+  int32_t r = L.t0 - 3 - dmask.row_lo;
   const uint32_t hs = doc_starts(dmask, r, 3);
   uint32_t hist = 0;
 #pragma unroll
@@ -822,49 +819,71 @@ void bwd_main_kernel(BwdArgs a) {
 
 // =================================================== backward reduce ==
 
-template <typename Acc>
-__device__ __forceinline__ void store_grad(void* dst, int64_t i, Acc v, int bf16);
-
-template <>
-__device__ __forceinline__ void store_grad<float>(void* dst, int64_t i, float v, int bf16) {
-  if (bf16) reinterpret_cast<uint16_t*>(dst)[i] = (uint16_t)bf16_bits_rne(v);
-  else reinterpret_cast<float*>(dst)[i] = v;
+// Sum over rows [r0, r1) of column o of a row-major [rows][n_out] matrix,
+// in a fixed order: the kRedChunks threads of output o take chunk q = rows
+// [r0 + q R, r0 + q R + R), R = ceil((r1 - r0) / kRedChunks), each in
+// increasing row order, and the chunk sums are added in increasing q.  The
+// sums are binary64 whatever the element type (binary32 partial rows under
+// "bf16", binary64 under "fp32"): a binary32 running sum over many rows
+// would lose digits in proportion to their count.  Every thread of the
+// workgroup calls this (one barrier); the result is valid in chunk 0.
+template <typename Part>
+__device__ __forceinline__ double sum_rows(const Part* m, int64_t n_out, int64_t o, int32_t r0,
+                                           int32_t r1, double (&red)[kRedChunks][kRedOut]) {
+  const int lane = threadIdx.x % kRedOut;
+  const int chunk = threadIdx.x / kRedOut;
+  const int32_t len = (r1 - r0 + kRedChunks - 1) / kRedChunks;
+  double s = 0.0;
+  if (o < n_out) {
+    const int32_t b0 = min(r0 + chunk * len, r1);
+    const int32_t b1 = min(b0 + len, r1);
+    const Part* p = m + (int64_t)b0 * n_out + o;
+#pragma unroll 8
+    for (int32_t b = b0; b < b1; ++b, p += n_out) s += (double)*p;
+  }
+  red[chunk][lane] = s;
+  __syncthreads();
+  double t = red[0][lane];
+#pragma unroll
+  for (int q = 1; q < kRedChunks; ++q) t += red[q][lane];
+  return t;
 }
 
-template <>
-__device__ __forceinline__ void store_grad<double>(void* dst, int64_t i, double v, int bf16) {
+// A gradient element: binary64 sum -> binary32 (round to nearest even) or
+// BF16 (rounded once, from the binary64 value).
+__device__ __forceinline__ void store_grad(void* dst, int64_t i, double v, int bf16) {
   if (bf16) reinterpret_cast<uint16_t*>(dst)[i] = bf16_bits_from_f64(v);
   else reinterpret_cast<float*>(dst)[i] = (float)v;
 }
 
-// out[o] = sum_{b=0..P-1} part[b][o] for o = k*C + c, in a fixed order:
-// chunk q sums rows [q*R, q*R+R) in increasing b, then the kRedChunks chunk
-// sums are added in increasing q.  The order depends on (P, C) only.
-template <typename Acc>
-__global__ __launch_bounds__(kRedOut * kRedChunks) void bwd_reduce_kernel(ReduceArgs a) {
-  __shared__ Acc red[kRedChunks][kRedOut];
-  const int lane = threadIdx.x % kRedOut;
-  const int chunk = threadIdx.x / kRedOut;
+// First stage (more than kRedBlockRows partial rows): workgroup (x, y) sums
+// rows [y kRedBlockRows, (y + 1) kRedBlockRows) of outputs
+// [x kRedOut, (x + 1) kRedOut) into inter[y][o].
+template <typename Part>
+__global__ __launch_bounds__(kRedOut * kRedChunks) void bwd_reduce_rows_kernel(ReduceArgs a) {
+  __shared__ double red[kRedChunks][kRedOut];
   const int64_t n_out = 5 * (int64_t)a.C;
-  const int64_t o = (int64_t)blockIdx.x * kRedOut + lane;
-  Acc s = (Acc)0;
-  if (o < n_out) {
-    const int32_t b0 = chunk * a.rows_per_chunk;
-    const int32_t b1 = min(b0 + a.rows_per_chunk, a.P);
-    const Acc* p = reinterpret_cast<const Acc*>(a.part) + (int64_t)b0 * n_out + o;
-#pragma unroll 8
-    for (int32_t b = b0; b < b1; ++b, p += n_out) s += *p;
-  }
-  red[chunk][lane] = s;
-  __syncthreads();
-  if (chunk == 0 && o < n_out) {
-    Acc t = red[0][lane];
-#pragma unroll
-    for (int q = 1; q < kRedChunks; ++q) t += red[q][lane];
+  const int64_t o = (int64_t)blockIdx.x * kRedOut + threadIdx.x % kRedOut;
+  const int32_t r0 = (int32_t)blockIdx.y * kRedBlockRows;
+  const int32_t r1 = min(r0 + kRedBlockRows, a.P);
+  const double t = sum_rows(reinterpret_cast<const Part*>(a.part), n_out, o, r0, r1, red);
+  if (threadIdx.x < kRedOut && o < n_out)
+    reinterpret_cast<double*>(a.inter)[(int64_t)blockIdx.y * n_out + o] = t;
+}
+
+// Final pass: out[o] = sum_{b=0..P-1} part[b][o] for o = k*C + c, rounded
+// once to the output dtype.  The order depends on (P, C) only.
+template <typename Part>
+__global__ __launch_bounds__(kRedOut * kRedChunks) void bwd_reduce_kernel(ReduceArgs a) {
+  __shared__ double red[kRedChunks][kRedOut];
+  const int64_t n_out = 5 * (int64_t)a.C;
+  const int64_t o = (int64_t)blockIdx.x * kRedOut + threadIdx.x % kRedOut;
+  const double t = sum_rows(reinterpret_cast<const Part*>(a.part), n_out, o, 0, a.P, red);
+  if (threadIdx.x < kRedOut && o < n_out) {
     const int64_t k = o / a.C;
     const int64_t c = o - k * a.C;
-    if (k < 4) store_grad<Acc>(a.dw, c * 4 + k, t, a.dw_bf16);
-    else if (a.db) store_grad<Acc>(a.db, c, t, a.db_bf16);
+    if (k < 4) store_grad(a.dw, c * 4 + k, t, a.dw_bf16);
+    else if (a.db) store_grad(a.db, c, t, a.db_bf16);
   }
 }
 
@@ -905,9 +924,17 @@ hipError_t launch_bwd_main(const Plan& plan, const BwdArgs& a, bool has_bias, bo
   return launch_bwd_main_v<kBwdVec>(plan, a, has_bias, fp32_policy, s);
 }
 
-hipError_t launch_bwd_reduce(const Plan& plan, const ReduceArgs& a, bool fp64, hipStream_t s) {
+hipError_t launch_bwd_reduce_rows(const Plan& plan, const ReduceArgs& a, bool part_f64,
+                                  hipStream_t s) {
+  dim3 grid(plan.red_blocks, plan.red_stage1), block(kRedOut * kRedChunks);
+  if (part_f64) hipLaunchKernelGGL(bwd_reduce_rows_kernel<double>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(bwd_reduce_rows_kernel<float>, grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_reduce(const Plan& plan, const ReduceArgs& a, bool part_f64, hipStream_t s) {
   dim3 grid(plan.red_blocks), block(kRedOut * kRedChunks);
-  if (fp64) hipLaunchKernelGGL(bwd_reduce_kernel<double>, grid, block, 0, s, a);
+  if (part_f64) hipLaunchKernelGGL(bwd_reduce_kernel<double>, grid, block, 0, s, a);
   else hipLaunchKernelGGL(bwd_reduce_kernel<float>, grid, block, 0, s, a);
   return hipGetLastError();
 }
