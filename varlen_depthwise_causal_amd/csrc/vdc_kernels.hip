@@ -370,10 +370,23 @@ constexpr SiluGradTable make_silu_grad_table() {
 __constant__ SiluGradTable kSiluGradTable = make_silu_grad_table();
 
 // Table index of BF16 bit pattern `bits` (16 bits, sign included).
-__device__ __forceinline__ uint32_t lut_index(uint32_t bits) {
-  uint32_t a = bits & 0x7fffu;
-  a = min(max(a, kLutLo), kLutHi);
-  return (a - kLutLo) + ((bits >> 15) & 1u) * uint32_t(kLutN);
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Byte offsets in the table of the two BF16 values packed in h (low half,
+// high half): 4 (clamp(magnitude) - kLutLo) + 4 kLutN sign.  Both halves
+// are formed in one 32-bit word: each half's offset stays below 2^16, so
+// the word's 32-bit sums carry nothing between the halves.
+static_assert(4 * 2 * kLutN < 65536, "table offsets must fit 16 bits");
+__device__ __forceinline__ void lut_offsets2(uint32_t h, uint32_t& off_lo, uint32_t& off_hi) {
+  constexpr uint32_t kLo2 = kLutLo * 0x10001u, kHi2 = kLutHi * 0x10001u;
+  u16x2 m = __builtin_bit_cast(u16x2, h & 0x7fff7fffu);
+  m = __builtin_elementwise_min(__builtin_elementwise_max(m, __builtin_bit_cast(u16x2, kLo2)),
+                                __builtin_bit_cast(u16x2, kHi2));
+  const uint32_t sign2 = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, h) >> (u16x2)(15));
+  const uint32_t o = (__builtin_bit_cast(uint32_t, m) << 2) +
+                     (sign2 * uint32_t(4 * kLutN) - 4u * kLo2);
+  off_lo = o & 0xffffu;
+  off_hi = o >> 16;
 }
 
 // ------------------------------------------------- the preactivation --
@@ -594,8 +607,11 @@ __device__ __forceinline__ void dpre_row(const float (&p)[V], const float (&dyv)
 #pragma unroll
     for (int d = 0; d < V / 2; ++d) {
       const uint32_t h = pack2(p[2 * d], p[2 * d + 1]);
-      dp[2 * d] = dyv[2 * d] * lut[lut_index(h & 0xffffu)];
-      dp[2 * d + 1] = dyv[2 * d + 1] * lut[lut_index(h >> 16)];
+      uint32_t o0, o1;
+      lut_offsets2(h, o0, o1);
+      const char* base = reinterpret_cast<const char*>(lut);
+      dp[2 * d] = dyv[2 * d] * *reinterpret_cast<const float*>(base + o0);
+      dp[2 * d + 1] = dyv[2 * d + 1] * *reinterpret_cast<const float*>(base + o1);
     }
   } else {
     float zmin = 0.0f;
