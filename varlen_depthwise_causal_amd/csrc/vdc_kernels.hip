@@ -141,51 +141,71 @@ __device__ __forceinline__ uint32_t span_bytes(int32_t S, int32_t C, int32_t row
 
 // ------------------------------------------------------- parameters --
 
-// weight [C][4] -> w[k][i] for the lane's channels c0 .. c0+V-1
-// (FP32: one 16-byte vector per channel; BF16: one 8-byte vector).
+// Parameters of the lane's channels c0 .. c0+V-1, loaded raw and unpacked
+// later, so that the loads can be issued first without their values being
+// waited for: weight [C][4] (FP32: one 16-byte vector per channel; BF16:
+// 8 bytes per channel, two channels per 16-byte vector) and bias [C] (FP32:
+// 16 bytes per 4 channels; BF16: 8 bytes).
 template <int V>
-__device__ __forceinline__ void load_weights(const void* w, int bf16, uint32_t c0,
-                                             float (&wk)[4][V]) {
-  if (!bf16) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(w) + c0;
+struct ParamRaw {
+  u32x4 w[V];
+  u32x4 b[V / 4];
+};
+
+template <int V>
+__device__ __forceinline__ void load_params(const void* w, int w_bf16, const void* b, int b_bf16,
+                                            bool has_bias, uint32_t c0, ParamRaw<V>& raw) {
+  static_assert(V == 4, "four channels per lane");
+  // The same loads for either dtype, at offsets chosen without a branch:
+  // a branch here makes the compiler copy loaded registers at its join, and
+  // each copy waits for its load.  BF16 weights take 32 bytes (two 16-byte
+  // loads, each issued twice); a BF16 bias 8 bytes (issued twice).
+  const char* pw = reinterpret_cast<const char*>(w);
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      u32x4 v = p[i];
-      wk[0][i] = __uint_as_float(v.x);
-      wk[1][i] = __uint_as_float(v.y);
-      wk[2][i] = __uint_as_float(v.z);
-      wk[3][i] = __uint_as_float(v.w);
-    }
+  for (int i = 0; i < V; ++i) {
+    const uint32_t off = w_bf16 ? c0 * 8u + 16u * (uint32_t)(i & 1) : c0 * 16u + 16u * (uint32_t)i;
+    raw.w[i] = *reinterpret_cast<const u32x4*>(pw + off);
+  }
+  if (has_bias) {
+    const char* pb = reinterpret_cast<const char*>(b);
+    const uint32_t off0 = b_bf16 ? c0 * 2u : c0 * 4u;
+    const uint32_t off1 = b_bf16 ? c0 * 2u : c0 * 4u + 8u;
+    const u32x2 lo = *reinterpret_cast<const u32x2*>(pb + off0);
+    const u32x2 hi = *reinterpret_cast<const u32x2*>(pb + off1);
+    raw.b[0] = (u32x4){lo.x, lo.y, hi.x, hi.y};
   } else {
-    const u32x2* p = reinterpret_cast<const u32x2*>(w) + c0;
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      u32x2 v = p[i];
-      wk[0][i] = bf_lo(v.x);
-      wk[1][i] = bf_hi(v.x);
-      wk[2][i] = bf_lo(v.y);
-      wk[3][i] = bf_hi(v.y);
-    }
+    raw.b[0] = (u32x4){0u, 0u, 0u, 0u};
   }
 }
 
 template <int V>
-__device__ __forceinline__ void load_bias(const void* b, int bf16, uint32_t c0, float (&bv)[V]) {
-  if (!bf16) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(b) + c0 / 4;
+__device__ __forceinline__ void unpack_params(const ParamRaw<V>& raw, int w_bf16, int b_bf16,
+                                              float (&wk)[4][V], float (&bv)[V]) {
 #pragma unroll
-    for (int q = 0; q < V / 4; ++q) {
-      u32x4 v = p[q];
+  for (int i = 0; i < V; ++i) {
+    if (!w_bf16) {
+      wk[0][i] = __uint_as_float(raw.w[i].x);
+      wk[1][i] = __uint_as_float(raw.w[i].y);
+      wk[2][i] = __uint_as_float(raw.w[i].z);
+      wk[3][i] = __uint_as_float(raw.w[i].w);
+    } else {
+      const u32x4 v = raw.w[(i / 2) & 1];
+      const uint32_t lo = (i & 1) ? v.z : v.x, hi = (i & 1) ? v.w : v.y;
+      wk[0][i] = bf_lo(lo);
+      wk[1][i] = bf_hi(lo);
+      wk[2][i] = bf_lo(hi);
+      wk[3][i] = bf_hi(hi);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < V / 4; ++q) {
+    const u32x4 v = raw.b[q];
+    if (!b_bf16) {
       bv[4 * q + 0] = __uint_as_float(v.x);
       bv[4 * q + 1] = __uint_as_float(v.y);
       bv[4 * q + 2] = __uint_as_float(v.z);
       bv[4 * q + 3] = __uint_as_float(v.w);
-    }
-  } else {
-    const u32x2* p = reinterpret_cast<const u32x2*>(b) + c0 / 4;
-#pragma unroll
-    for (int q = 0; q < V / 4; ++q) {
-      u32x2 v = p[q];
+    } else {
       bv[4 * q + 0] = bf_lo(v.x);
       bv[4 * q + 1] = bf_hi(v.x);
       bv[4 * q + 2] = bf_lo(v.y);
@@ -229,13 +249,20 @@ struct DocMask {
   int32_t idx_lo, idx_hi;            // cu_seqlens entries that fall in the rows
 };
 
+// With fewer documents than threads, each thread reads one entry of
+// cu_seqlens up front (issued before the activation loads, so waiting for
+// it waits for nothing else); with more, the entries are found by search.
+__device__ __forceinline__ int32_t doc_mask_prefetch(const int32_t* cu, int32_t num_docs) {
+  return (num_docs < kBlock && (int32_t)threadIdx.x <= num_docs) ? cu[threadIdx.x] : -1;
+}
+
 // Every thread of the workgroup must call this (two barriers).  The rows
 // touched are the workgroup's bands plus three halo rows on each side; the
 // last band's rows may run past S (and past 2^31 - 1), where no start
 // matters, so only starts below S are marked.
-__device__ __forceinline__ void build_doc_mask(DocMask& m, const int32_t* cu, int32_t num_docs,
-                                               int32_t S, int32_t nvec, int32_t rows,
-                                               int32_t bands) {
+__device__ __forceinline__ void build_doc_mask(DocMask& m, int32_t t_pre, const int32_t* cu,
+                                               int32_t num_docs, int32_t S, int32_t nvec,
+                                               int32_t rows, int32_t bands) {
   const int32_t g0 = (int32_t)blockIdx.x * kBlock;
   const int32_t first_band = g0 / nvec;
   const int32_t last_band = min((g0 + kBlock - 1) / nvec, bands - 1);
@@ -244,6 +271,18 @@ __device__ __forceinline__ void build_doc_mask(DocMask& m, const int32_t* cu, in
   // At most kDocMaskWords + 1 words by the host's choice of rows.
   const int32_t nwords = (int32_t)((row_end - row_lo) >> 5) + 2;
   const int32_t row_hi = (int32_t)min(row_end, (int64_t)S);
+  const int32_t first_row = max(row_lo, 0);
+  if (num_docs < kBlock) {
+    // Few documents: the entry this thread read up front, no search.
+    const int32_t t = t_pre;
+    for (int32_t i = threadIdx.x; i < nwords; i += kBlock) m.bits[i] = 0u;
+    if (threadIdx.x == 0) m.row_lo = row_lo;
+    __syncthreads();
+    if (t >= first_row && t < row_hi)
+      atomicOr(&m.bits[(t - row_lo) >> 5], 1u << ((t - row_lo) & 31));
+    __syncthreads();
+    return;
+  }
   for (int32_t i = threadIdx.x; i < nwords; i += kBlock) m.bits[i] = 0u;
   if (threadIdx.x < 64) {
     const int32_t lo = wave_lower_bound(cu, num_docs + 1, max(row_lo, 0));
@@ -255,7 +294,6 @@ __device__ __forceinline__ void build_doc_mask(DocMask& m, const int32_t* cu, in
     }
   }
   __syncthreads();
-  const int32_t first_row = max(row_lo, 0);
   for (int32_t i = m.idx_lo + (int32_t)threadIdx.x; i < m.idx_hi; i += kBlock) {
     const int32_t t = cu[i];
     if (t >= first_row && t < row_hi)
@@ -350,7 +388,7 @@ constexpr float cx_silu_grad(double z) {
   return float(s * (1.0 + z * one_minus_s));
 }
 
-struct SiluGradTable {
+struct alignas(16) SiluGradTable {
   float v[2 * kLutN];  // [0, N): +z, [N, 2N): -z, index = magnitude pattern - kLutLo
 };
 
@@ -368,6 +406,35 @@ constexpr SiluGradTable make_silu_grad_table() {
 }
 
 __constant__ SiluGradTable kSiluGradTable = make_silu_grad_table();
+
+// Staging of the table into LDS by a whole workgroup: 16-byte loads, all
+// issued before any is waited for (a loop of one load and one store per
+// element would wait out a memory round trip per element).
+constexpr int kLutQuads = 2 * kLutN / 4;
+constexpr int kLutStageIters = (kLutQuads + kBlock - 1) / kBlock;
+static_assert(2 * kLutN % 4 == 0, "the table is staged in 16-byte pieces");
+
+struct LutStage {
+  u32x4 q[kLutStageIters];
+};
+
+__device__ __forceinline__ void lut_stage_load(LutStage& st) {
+  const u32x4* src = reinterpret_cast<const u32x4*>(kSiluGradTable.v);
+#pragma unroll
+  for (int k = 0; k < kLutStageIters; ++k) {
+    const int i = (int)threadIdx.x + k * kBlock;
+    if (i < kLutQuads) st.q[k] = src[i];
+  }
+}
+
+__device__ __forceinline__ void lut_stage_store(const LutStage& st, float* lds) {
+  u32x4* dst = reinterpret_cast<u32x4*>(lds);
+#pragma unroll
+  for (int k = 0; k < kLutStageIters; ++k) {
+    const int i = (int)threadIdx.x + k * kBlock;
+    if (i < kLutQuads) dst[i] = st.q[k];
+  }
+}
 
 // Table index of BF16 bit pattern `bits` (16 bits, sign included).
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
@@ -474,6 +541,12 @@ void fwd_kernel(FwdArgs a) {
   __shared__ DocMask dmask;
   Lane L;
   const bool active = lane_coords<V>(a.nvec, a.rows, a.bands, a.C, L);
+  // Parameters and the document starts are requested before the
+  // activations: loads complete in issue order, so waiting for these waits
+  // for no activation row.
+  ParamRaw<V> praw;
+  load_params<V>(a.w, a.w_bf16, a.b, a.b_bf16, kBias, L.vec * V, praw);
+  const int32_t cu_pre = doc_mask_prefetch(a.cu, a.num_docs);
   const int32_t row_bytes = a.C * 2;
   const uint32_t nrec = span_bytes(a.S, a.C, L.base_row);  // wave-uniform
   const rsrc_t rx = make_rsrc(a.x + (int64_t)L.base_row * a.C, nrec);
@@ -486,20 +559,19 @@ void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int q = 0; q < 3; ++q) halo[q] = VT::zero();
   off += 3 * row_bytes;
-  if (active) {
+  // Unconditional, so that no wait on the table or mask loads issued later
+  // has to cover a path without them: rows before row 0 have negative
+  // offsets, which the buffer range check reads as zero, and lanes past the
+  // last band read rows of the last band, then leave.
 #pragma unroll
-    for (int q = 0; q < 3; ++q)
-      if (L.t0 - 3 + q >= 0) halo[q] = VT::load(rx, off + (q - 3) * row_bytes);
+  for (int q = 0; q < 3; ++q) halo[q] = VT::load(rx, off + (q - 3) * row_bytes);
 #pragma unroll
-    for (int g = 0; g < kFwdGroup; ++g) A[g] = VT::load(rx, off + g * row_bytes);
-  }
+  for (int g = 0; g < kFwdGroup; ++g) A[g] = VT::load(rx, off + g * row_bytes);
 
-  build_doc_mask(dmask, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
+  build_doc_mask(dmask, cu_pre, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
   if (!active) return;
-
   float w[4][V], bv[V];
-  load_weights<V>(a.w, a.w_bf16, L.vec * V, w);
-  if (kBias) load_bias<V>(a.b, a.b_bf16, L.vec * V, bv);
+  unpack_params<V>(praw, a.w_bf16, a.b_bf16, w, bv);
 
   // Window of the three previous rows: h1 = x[r-1], h2 = x[r-2], h3 = x[r-3].
   float h1[V], h2[V], h3[V];
@@ -686,10 +758,18 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kBwdWave
 void bwd_main_kernel(BwdArgs a) {
   typedef Vec<V> VT;
   typedef typename VT::raw Raw;
-  __shared__ float lut_lds[kBf16Policy ? 2 * kLutN : 1];
+  __shared__ __attribute__((aligned(16))) float lut_lds[kBf16Policy ? 2 * kLutN : 4];
   __shared__ DocMask dmask;
   Lane L;
   const bool active = lane_coords<V>(a.nvec, a.rows, a.bands, a.C, L);
+  // Parameters, the SiLU' table and the document starts are requested
+  // before the activations: loads complete in issue order, so waiting for
+  // these waits for no activation row.
+  ParamRaw<V> praw;
+  load_params<V>(a.w, a.w_bf16, a.b, a.b_bf16, kBias, L.vec * V, praw);
+  LutStage lut_stage;
+  if (kBf16Policy) lut_stage_load(lut_stage);
+  const int32_t cu_pre = doc_mask_prefetch(a.cu, a.num_docs);
   const int32_t row_bytes = a.C * 2;
   const uint32_t nrec = span_bytes(a.S, a.C, L.base_row);  // wave-uniform
   const int64_t base_elt = (int64_t)L.base_row * a.C;
@@ -704,28 +784,26 @@ void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
   for (int q = 0; q < 3; ++q) halo[q] = VT::zero();
   off += 3 * row_bytes;
-  if (active) {
+  // Unconditional, so that no wait on the table or mask loads issued later
+  // has to cover a path without them: rows before row 0 have negative
+  // offsets, which the buffer range check reads as zero, and lanes past the
+  // last band read rows of the last band, then leave.
 #pragma unroll
-    for (int q = 0; q < 3; ++q)
-      if (L.t0 - 3 + q >= 0) halo[q] = VT::load(rx, off + (q - 3) * row_bytes);
+  for (int q = 0; q < 3; ++q) halo[q] = VT::load(rx, off + (q - 3) * row_bytes);
 #pragma unroll
-    for (int g = 0; g < kBwdGroup; ++g) {
-      xa[g] = VT::load(rx, off + g * row_bytes);
-      da[g] = VT::load(rdy, off + g * row_bytes);
-    }
+  for (int g = 0; g < kBwdGroup; ++g) {
+    xa[g] = VT::load(rx, off + g * row_bytes);
+    da[g] = VT::load(rdy, off + g * row_bytes);
   }
 
-  if (kBf16Policy) {
-    // Every thread helps to stage the SiLU' table (the mask builder's
-    // barriers make it visible).
-    for (int i = threadIdx.x; i < 2 * kLutN; i += kBlock) lut_lds[i] = kSiluGradTable.v[i];
-  }
-  build_doc_mask(dmask, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
+  // Every thread stages its part of the SiLU' table (the mask builder's
+  // barriers make it visible).
+  if (kBf16Policy) lut_stage_store(lut_stage, lut_lds);
+  build_doc_mask(dmask, cu_pre, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
   if (!active) return;
-
   float w[4][V], bv[V];
-  load_weights<V>(a.w, a.w_bf16, L.vec * V, w);
-  if (kBias) load_bias<V>(a.b, a.b_bf16, L.vec * V, bv);
+  unpack_params<V>(praw, a.w_bf16, a.b_bf16, w, bv);
+
   Partials<Acc, V> acc;
 #pragma unroll
   for (int k = 0; k < 5; ++k)
