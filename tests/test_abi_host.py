@@ -156,7 +156,7 @@ def test_plans_depend_on_shape_only(lib):
             assert lib.conv1d_plan(d, S, C, 0, b) == OK
             assert list(a) == list(b)
             rows, bands, lanes, blocks, threads, vec = a[0], a[1], a[2], a[3], a[4], a[8]
-            assert vec in (4, 8) and C % vec == 0
+            assert vec == 4 and C % vec == 0
             assert rows % 8 == 0 and rows >= 16
             assert lanes == bands * (C // vec) and blocks * threads >= lanes
             # a wave's span of rows stays far inside 32-bit byte offsets

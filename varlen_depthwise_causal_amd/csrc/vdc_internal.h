@@ -9,13 +9,6 @@
 
 namespace vdc {
 
-// Channels one lane owns (a vector of 4 or 8 BF16 values), per direction.
-#ifndef VDC_FWD_VEC
-#define VDC_FWD_VEC 4
-#endif
-#ifndef VDC_BWD_VEC
-#define VDC_BWD_VEC 4
-#endif
 // Waves per SIMD each kernel is built for (register budget) and planned
 // for: one, with a deep double-buffered load pipeline per wave.
 #ifndef VDC_FWD_WAVES
@@ -26,8 +19,9 @@ namespace vdc {
 #endif
 constexpr int kFwdWaves = VDC_FWD_WAVES;
 constexpr int kBwdWaves = VDC_BWD_WAVES;
-constexpr int kFwdVec = VDC_FWD_VEC;
-constexpr int kBwdVec = VDC_BWD_VEC;
+// Channels one lane owns: 4 BF16 values, one 8-byte vector per row.
+constexpr int kFwdVec = 4;
+constexpr int kBwdVec = 4;
 // Threads per workgroup of the main kernels (four wave64).
 constexpr int kBlock = 256;
 // Rows per load group (two groups are in flight per lane).

@@ -85,19 +85,9 @@ __device__ __forceinline__ uint16_t bf16_bits_from_f64(double d) {
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// ------------------------------------------------ lane vectors (V = 4, 8) --
+// ------------------------------------------------------ lane vectors --
 
 template <int V> struct Vec;
-template <> struct Vec<8> {
-  typedef u32x4 raw;
-  __device__ static __forceinline__ raw load(rsrc_t r, int32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream);
-  }
-  __device__ static __forceinline__ void store(rsrc_t r, int32_t off, raw v) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStream);
-  }
-  __device__ static __forceinline__ raw zero() { return (raw){0u, 0u, 0u, 0u}; }
-};
 template <> struct Vec<4> {
   typedef u32x2 raw;
   __device__ static __forceinline__ raw load(rsrc_t r, int32_t off) {
