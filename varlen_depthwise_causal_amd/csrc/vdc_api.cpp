@@ -102,7 +102,9 @@ Plan make_plan(int dir, int64_t S, int64_t C, int policy) {
 }
 
 // Lane and workgroup indices are 32-bit in the kernels.
-bool plan_fits(const Plan& p) { return p.lanes <= (int64_t)INT32_MAX - kBlock; }
+bool plan_fits(const Plan& p) {
+  return p.lanes <= (int64_t)INT32_MAX - kXcds * kBlock && padded_grid(p.blocks) <= INT32_MAX;
+}
 
 int check_sizes(int64_t S, int64_t C, int64_t num_docs) {
   if (C <= 0 || C % 8 != 0 || C > kMaxC) return VDC_EINVAL;
@@ -190,6 +192,7 @@ extern "C" int conv1d_fwd(const void* x, const void* weight, int w_dtype, const 
   a.nvec = (int32_t)(C / plan.vec);
   a.rows = plan.rows;
   a.bands = plan.bands;
+  a.blocks = plan.blocks;
   g_launches.fetch_add(1, std::memory_order_relaxed);
   return launch_fwd(plan, a, bias != nullptr, stream) == hipSuccess ? VDC_OK : VDC_EHIP;
 }
@@ -280,6 +283,7 @@ extern "C" int conv1d_bwd(const void* x, const void* weight, int w_dtype, const 
   a.nvec = (int32_t)(C / plan.vec);
   a.rows = plan.rows;
   a.bands = plan.bands;
+  a.blocks = plan.blocks;
   g_launches.fetch_add(1, std::memory_order_relaxed);
   if (launch_bwd_main(plan, a, bias != nullptr, fp32_policy, stream) != hipSuccess) return VDC_EHIP;
 

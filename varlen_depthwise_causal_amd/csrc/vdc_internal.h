@@ -39,6 +39,17 @@ constexpr int kBwdGroup = VDC_BWD_GROUP;
 // fewer than 32 * (kDocMaskWords - 1) rows.
 constexpr int kDocMaskWords = 1024;
 
+// Workgroup placement: 1 = neighbouring workgroups of the lane order on one
+// XCD (grid padded to a multiple of 8), 0 = hardware order.
+#ifndef VDC_XCD_REMAP
+#define VDC_XCD_REMAP 1
+#endif
+constexpr int kXcds = 8;
+
+inline int64_t padded_grid(int64_t blocks) {
+  return VDC_XCD_REMAP ? (blocks + kXcds - 1) / kXcds * kXcds : blocks;
+}
+
 constexpr int kRedOut = 64;
 constexpr int kRedChunks = 8;
 // Partial rows one first-stage reduce workgroup sums.  With more rows than
@@ -73,6 +84,7 @@ struct FwdArgs {
   int32_t nvec;        // C / V
   int32_t rows;        // T
   int32_t bands;
+  int32_t blocks;      // workgroups with lanes (the grid may be padded)
 };
 
 struct BwdArgs {
@@ -91,6 +103,7 @@ struct BwdArgs {
   int32_t nvec;
   int32_t rows;
   int32_t bands;
+  int32_t blocks;      // workgroups with lanes (the grid may be padded)
 };
 
 struct ReduceArgs {

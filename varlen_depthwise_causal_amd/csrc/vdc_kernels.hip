@@ -250,10 +250,10 @@ __device__ __forceinline__ int32_t doc_mask_prefetch(const int32_t* cu, int32_t 
 // touched are the workgroup's bands plus three halo rows on each side; the
 // last band's rows may run past S (and past 2^31 - 1), where no start
 // matters, so only starts below S are marked.
-__device__ __forceinline__ void build_doc_mask(DocMask& m, int32_t t_pre, const int32_t* cu,
-                                               int32_t num_docs, int32_t S, int32_t nvec,
-                                               int32_t rows, int32_t bands) {
-  const int32_t g0 = (int32_t)blockIdx.x * kBlock;
+__device__ __forceinline__ void build_doc_mask(DocMask& m, uint32_t place, int32_t t_pre,
+                                               const int32_t* cu, int32_t num_docs, int32_t S,
+                                               int32_t nvec, int32_t rows, int32_t bands) {
+  const int32_t g0 = (int32_t)place * kBlock;
   const int32_t first_band = g0 / nvec;
   const int32_t last_band = min((g0 + kBlock - 1) / nvec, bands - 1);
   const int32_t row_lo = first_band * rows - 3;
@@ -469,10 +469,22 @@ struct Lane {
   int32_t off;       // byte offset of (t0 - 3, vec) from the base
 };
 
+// The workgroup's place in the lane order.  Workgroups are dispatched to
+// the XCDs round-robin (workgroup i to XCD i mod 8), and each XCD has its
+// own L2.  With the grid padded to a multiple of 8, workgroup i takes place
+// (i mod 8) (grid / 8) + i / 8, so that neighbouring places sit on one XCD:
+// they share the cache lines at their boundary whenever a row is not a
+// multiple of 128 bytes, and one L2 then fetches each such line once.
+__device__ __forceinline__ uint32_t block_place() {
+  if (!VDC_XCD_REMAP) return blockIdx.x;
+  const uint32_t per = gridDim.x / kXcds;
+  return (blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+}
+
 template <int V>
-__device__ __forceinline__ bool lane_coords(int32_t nvec, int32_t rows, int32_t bands, int32_t C,
-                                            Lane& L) {
-  const uint32_t g = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
+__device__ __forceinline__ bool lane_coords(uint32_t place, int32_t nvec, int32_t rows,
+                                            int32_t bands, int32_t C, Lane& L) {
+  const uint32_t g = place * (uint32_t)kBlock + threadIdx.x;
   const uint32_t band = g / (uint32_t)nvec;
   const bool active = band < (uint32_t)bands;
   // Lanes past the last band keep the last band's coordinates (they load
@@ -530,7 +542,9 @@ void fwd_kernel(FwdArgs a) {
   typedef typename VT::raw Raw;
   __shared__ DocMask dmask;
   Lane L;
-  const bool active = lane_coords<V>(a.nvec, a.rows, a.bands, a.C, L);
+  const uint32_t place = block_place();
+  if (place >= (uint32_t)a.blocks) return;  // padding workgroup: no lane
+  const bool active = lane_coords<V>(place, a.nvec, a.rows, a.bands, a.C, L);
   // Parameters and the document starts are requested before the
   // activations: loads complete in issue order, so waiting for these waits
   // for no activation row.
@@ -558,7 +572,7 @@ void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int g = 0; g < kFwdGroup; ++g) A[g] = VT::load(rx, off + g * row_bytes);
 
-  build_doc_mask(dmask, cu_pre, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
+  build_doc_mask(dmask, place, cu_pre, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
   if (!active) return;
   float w[4][V], bv[V];
   unpack_params<V>(praw, a.w_bf16, a.b_bf16, w, bv);
@@ -751,7 +765,9 @@ void bwd_main_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float lut_lds[kBf16Policy ? 2 * kLutN : 4];
   __shared__ DocMask dmask;
   Lane L;
-  const bool active = lane_coords<V>(a.nvec, a.rows, a.bands, a.C, L);
+  const uint32_t place = block_place();
+  if (place >= (uint32_t)a.blocks) return;  // padding workgroup: no lane
+  const bool active = lane_coords<V>(place, a.nvec, a.rows, a.bands, a.C, L);
   // Parameters, the SiLU' table and the document starts are requested
   // before the activations: loads complete in issue order, so waiting for
   // these waits for no activation row.
@@ -789,7 +805,7 @@ void bwd_main_kernel(BwdArgs a) {
   // Every thread stages its part of the SiLU' table (the mask builder's
   // barriers make it visible).
   if (kBf16Policy) lut_stage_store(lut_stage, lut_lds);
-  build_doc_mask(dmask, cu_pre, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
+  build_doc_mask(dmask, place, cu_pre, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
   if (!active) return;
   float w[4][V], bv[V];
   unpack_params<V>(praw, a.w_bf16, a.b_bf16, w, bv);
@@ -973,7 +989,7 @@ __global__ __launch_bounds__(kRedOut * kRedChunks) void bwd_reduce_kernel(Reduce
 
 template <int V>
 hipError_t launch_fwd_v(const Plan& plan, const FwdArgs& a, bool has_bias, hipStream_t s) {
-  dim3 grid(plan.blocks), block(kBlock);
+  dim3 grid((uint32_t)padded_grid(plan.blocks)), block(kBlock);
   if (has_bias) hipLaunchKernelGGL((fwd_kernel<true, V>), grid, block, 0, s, a);
   else hipLaunchKernelGGL((fwd_kernel<false, V>), grid, block, 0, s, a);
   return hipGetLastError();
@@ -982,7 +998,7 @@ hipError_t launch_fwd_v(const Plan& plan, const FwdArgs& a, bool has_bias, hipSt
 template <int V>
 hipError_t launch_bwd_main_v(const Plan& plan, const BwdArgs& a, bool has_bias, bool fp32_policy,
                              hipStream_t s) {
-  dim3 grid(plan.blocks), block(kBlock);
+  dim3 grid((uint32_t)padded_grid(plan.blocks)), block(kBlock);
   if (fp32_policy) {
     if (has_bias) hipLaunchKernelGGL((bwd_main_kernel<true, false, double, V>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((bwd_main_kernel<false, false, double, V>), grid, block, 0, s, a);
