@@ -33,7 +33,6 @@ constexpr int kBlock = 256;
 #endif
 constexpr int kFwdGroup = VDC_FWD_GROUP;
 constexpr int kBwdGroup = VDC_BWD_GROUP;
-// Reduce kernel: outputs per workgroup and row chunks (one wave each).
 // Document-start bitmask of one workgroup, in 32-bit LDS words: the rows a
 // workgroup touches (its bands and three halo rows on each side) must span
 // fewer than 32 * (kDocMaskWords - 1) rows.
@@ -50,6 +49,7 @@ inline int64_t padded_grid(int64_t blocks) {
   return VDC_XCD_REMAP ? (blocks + kXcds - 1) / kXcds * kXcds : blocks;
 }
 
+// Reduce kernels: outputs per workgroup and row chunks (one wave each).
 constexpr int kRedOut = 64;
 constexpr int kRedChunks = 8;
 // Partial rows one first-stage reduce workgroup sums.  With more rows than

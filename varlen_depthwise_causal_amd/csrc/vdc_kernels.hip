@@ -8,20 +8,23 @@
 // it is bound by HBM traffic and VALU issue, not by matrix throughput: no
 // MFMA here.
 //
-// Work decomposition (same for every kernel of the main path):
-//  * A lane owns V consecutive BF16 channels (one 8- or 16-byte vector) and
-//    a band of T consecutive tokens, and walks the band row by row.  Lanes
-//    are numbered (band, vector) -> band * (C/V) + vector, so the 64 lanes of
-//    a wave read 64 consecutive vectors of a row (fully coalesced) and, when
-//    C/V is not a multiple of 64, simply continue into the next band.
+// Work decomposition (same for both main kernels):
+//  * A lane owns V = 4 consecutive BF16 channels (one 8-byte vector) and a
+//    band of T consecutive tokens, and walks the band row by row.  Lanes are
+//    numbered (band, vector) -> band * (C/4) + vector, so the 64 lanes of a
+//    wave read 64 consecutive vectors of a row (fully coalesced) and, when
+//    C/4 is not a multiple of 64, simply continue into the next band.
+//  * The kernels run one wave per SIMD and the host picks T so that all
+//    waves fit the machine at once; each wave double-buffers groups of
+//    rows in registers and stores a group's outputs after its last row.
 //  * A lane keeps the previous three rows of x in registers; at a document
 //    start the window is cleared, which is exactly the zero history the
-//    forward prescribes, so no tap needs a mask.  The document starts are
-//    found by one binary search of cu_seqlens per lane and a forward walk;
-//    groups of rows with no start nearby take a branch without any check.
+//    forward prescribes, so no tap needs a mask.  Each workgroup marks the
+//    document starts of its rows in an LDS bitmask; groups of rows with no
+//    start nearby take a branch without any check.
 //  * Tensors are addressed through buffer resources based at the wave's
-//    first row, with 32-bit per-lane offsets: rows past S read as zero and
-//    their stores are dropped by the hardware range check.
+//    first row, with 32-bit per-lane offsets: rows outside [0, S) read as
+//    zero and their stores are dropped by the hardware range check.
 //  * Arithmetic is FP32 with one fixed evaluation order for the
 //    preactivation, shared by the forward and the backward recompute, so
 //    both see the same bits of p.
@@ -130,9 +133,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                            kRsrcWord3);
 }
 
-// Bytes from row `row` to the end of an [S][C] BF16 tensor, clamped to what
-// a buffer resource can describe.  The host keeps a wave's whole span far
-// below 2^31 bytes, so the clamp only ever applies far from the end.
+// Bytes from row `row` to the end of an [S][C] BF16 tensor, clamped below
+// 2^31.  The clamp keeps every negative 32-bit offset (a row before the
+// base) out of range, so such rows read as zero; the host keeps a wave's
+// whole span far below 2^31 bytes, so the clamp never cuts a row the wave
+// uses.
 __device__ __forceinline__ uint32_t span_bytes(int32_t S, int32_t C, int32_t row) {
   uint64_t rem = (uint64_t)(int64_t)(S - row) * (uint64_t)C * 2u;
   return rem > 0xffffffffull ? 0xffffffffu : (uint32_t)rem;
@@ -217,11 +222,13 @@ __device__ __forceinline__ void unpack_params(const ParamRaw<V>& raw, int w_bf16
 //
 // A row t is a document start when t equals a value of cu_seqlens below S
 // (an empty document repeats its successor's start).  Each workgroup marks
-// the starts among the rows its lanes touch in an LDS bitmask: its first
-// wave finds the range of cu_seqlens entries with two 64-ary searches and
-// the whole workgroup sets the bits.  A lane then reads the starts of a
-// group of rows with two LDS loads, however many documents it holds.
-// The host sizes bands so that a workgroup's rows fit the bitmask.
+// the starts among the rows its lanes touch in an LDS bitmask.  With fewer
+// documents than threads every thread reads one entry of cu_seqlens; with
+// more, the first wave finds the range of entries that fall in the rows
+// with two 64-ary searches, and the whole workgroup reads that range.  A
+// lane then reads the starts of a group of rows with two LDS loads,
+// however many documents it holds.  The host sizes bands so that a
+// workgroup's rows fit the bitmask.
 
 // First index i in [0, n) with cu[i] >= v (n if none), by a whole wave:
 // each round probes 64 evenly spaced entries and keeps the bracket, so the
