@@ -134,13 +134,40 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 
 // Bytes from row `row` to the end of an [S][C] BF16 tensor, clamped below
-// 2^31.  The clamp keeps every negative 32-bit offset (a row before the
-// base) out of range, so such rows read as zero; the host keeps a wave's
-// whole span far below 2^31 bytes, so the clamp never cuts a row the wave
-// uses.
+// 2^31.  The clamp keeps every negative 32-bit offset out of range, so a
+// load there reads zero and a store there is dropped, without a memory
+// access; the host keeps a wave's whole span below 2^31 bytes, so the clamp
+// never cuts a row the wave uses.
 __device__ __forceinline__ uint32_t span_bytes(int32_t S, int32_t C, int32_t row) {
   uint64_t rem = (uint64_t)(int64_t)(S - row) * (uint64_t)C * 2u;
-  return rem > 0xffffffffull ? 0xffffffffu : (uint32_t)rem;
+  return rem > 0x7fffffffull ? 0x7fffffffu : (uint32_t)rem;
+}
+
+// Offset of "no row": loads there read zero, stores are dropped (see
+// span_bytes); kNoRow + g * row_bytes stays negative for every row group.
+// The main loops issue the same memory instructions on every path and send
+// the accesses they do not need here.  The compiler counts outstanding
+// accesses per path to place its waits, and takes the smallest count where
+// paths meet: an access skipped on one path would make every later wait
+// also wait for younger accesses that are still in flight.
+constexpr int32_t kNoRow = INT32_MIN;
+
+// Wait until at most N vector memory accesses of this wave are in flight
+// (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their
+// maxima, so they are not waited for).
+//
+// The main loops use it to pace themselves: once per pair of row groups a
+// wave waits until everything but the next group's loads has retired,
+// stores included.  Without that wait each wave runs at its own pace, the
+// rows in flight across the machine drift apart, and the memory side loses
+// efficiency: at 8 KiB rows the L2's read latency to memory grows by about a
+// quarter, its DRAM credit stalls grow four- to fivefold, and the kernels
+// lose 5-11%.  Issuing the next group's loads before the stores of the
+// group just computed (more accesses in flight per wave) is slower still.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // ------------------------------------------------------- parameters --
@@ -582,12 +609,21 @@ void fwd_kernel(FwdArgs a) {
   off += 3 * row_bytes;
   // Unconditional, so that no wait on the table or mask loads issued later
   // has to cover a path without them: rows before row 0 have negative
-  // offsets, which the buffer range check reads as zero, and lanes past the
-  // last band read rows of the last band, then leave.
+  // offsets, which read as zero, and lanes past the last band read rows of
+  // the last band, then leave.  The loads are issued in row order (kept by
+  // scheduling barriers), and dropped stores stand for the previous group's
+  // y rows: the loop is then entered with the same accesses in flight, in
+  // the same order, as from its own back edge.
 #pragma unroll
   for (int q = 0; q < 3; ++q) halo[q] = IO::load(rx, off + (q - 3) * row_bytes);
 #pragma unroll
-  for (int g = 0; g < kFwdGroup; ++g) A[g] = IO::load(rx, off + g * row_bytes);
+  for (int g = 0; g < kFwdGroup; ++g) {
+    __builtin_amdgcn_sched_barrier(0);
+    A[g] = IO::load(rx, off + g * row_bytes);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < kFwdGroup; ++g) IO::store(ry, kNoRow + g * row_bytes, VT::zero());
 
   build_doc_mask(dmask, place, cu_pre, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
   if (!active) return;
@@ -614,16 +650,14 @@ void fwd_kernel(FwdArgs a) {
   r += 3;
 
   // Groups of G rows, two register buffers: the loads of group k+1 are in
-  // flight while group k is computed; a group's y rows are stored together
-  // after its last row (loads and stores share one wait counter on this
-  // architecture, so a store between loads would stall the next wait).
+  // flight while group k is computed, and a group's y rows are stored
+  // together after its last row (loads and stores share one wait counter on
+  // this architecture, so a store between loads would stall the next wait).
   auto load = [&](Raw (&buf)[kFwdGroup], int32_t at) {
 #pragma unroll
     for (int g = 0; g < kFwdGroup; ++g) buf[g] = IO::load(rx, at + g * row_bytes);
   };
-  auto run = [&](const Raw (&buf)[kFwdGroup]) {
-    // y goes to its own registers: the loaded rows stay read-only.
-    Raw out[kFwdGroup];
+  auto compute = [&](const Raw (&buf)[kFwdGroup], Raw (&out)[kFwdGroup]) {
     const uint32_t starts = doc_starts(dmask, r, kFwdGroup);
     if (starts == 0u) {
       // No document starts in this group.
@@ -649,17 +683,25 @@ void fwd_kernel(FwdArgs a) {
         for (int i = 0; i < V; ++i) h3[i] = h2[i], h2[i] = h1[i], h1[i] = xc[i];
       }
     }
+    r += kFwdGroup;
+  };
+  auto store = [&](const Raw (&out)[kFwdGroup]) {
 #pragma unroll
     for (int g = 0; g < kFwdGroup; ++g) IO::store(ry, off + g * row_bytes, out[g]);
-    r += kFwdGroup;
     off += kFwdGroup * row_bytes;
   };
-  // T is a multiple of 2G (host rule).
+  // T is a multiple of 2G (host rule).  The last pair's reload of A reads
+  // nothing (kNoRow).  y goes to its own registers: the loaded rows stay
+  // read-only.
+  Raw out[kFwdGroup];
   for (int32_t done = 0; done < a.rows; done += 2 * kFwdGroup) {
     load(B, off + kFwdGroup * row_bytes);
-    run(A);
-    if (done + 2 * kFwdGroup < a.rows) load(A, off + kFwdGroup * row_bytes);
-    run(B);
+    wait_vm<kFwdGroup>();  // pace: only B's loads remain in flight
+    compute(A, out);
+    store(out);
+    load(A, done + 2 * kFwdGroup < a.rows ? off + kFwdGroup * row_bytes : kNoRow);
+    compute(B, out);
+    store(out);
   }
 }
 
@@ -667,7 +709,7 @@ void fwd_kernel(FwdArgs a) {
 
 // A lane's gradient partials: taps k = 0..3, then the bias term.  The rows
 // of one row group (G rows) are summed in binary32 in `run`, and each
-// group's sum is added into the band totals `v`: binary64 under the "fp32"
+// group's sum is added into the band totals: binary64 under the "fp32"
 // policy (Acc = double), binary32 under "bf16" (Acc = float).  A run of G
 // products rounds within a few units in the last place of its own
 // magnitude; the totals then take T/G additions instead of T, which bounds
@@ -676,20 +718,26 @@ void fwd_kernel(FwdArgs a) {
 // of the binary64 operations of a per-row binary64 sum.
 template <typename Acc, int V>
 struct Partials {
-  Acc v[5][V];
   float run[5][V];
+  Acc v[5][V];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+#pragma unroll
+      for (int i = 0; i < V; ++i) run[k][i] = 0.0f, v[k][i] = (Acc)0;
+  }
+  __device__ __forceinline__ void fold() {
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        v[k][i] += (Acc)run[k][i];
+        run[k][i] = 0.0f;
+      }
+  }
+  __device__ __forceinline__ Acc total(int k, int i) const { return v[k][i]; }
 };
 
-template <typename Acc, int V>
-__device__ __forceinline__ void fold_partials(Partials<Acc, V>& acc) {
-#pragma unroll
-  for (int k = 0; k < 5; ++k)
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      acc.v[k][i] += (Acc)acc.run[k][i];
-      acc.run[k][i] = 0.0f;
-    }
-}
 
 // dpre = dy * SiLU'(z) for the lane's V channels of one row.
 template <bool kBf16Policy, int V>
@@ -810,15 +858,22 @@ void bwd_main_kernel(BwdArgs a) {
   off += 3 * row_bytes;
   // Unconditional, so that no wait on the table or mask loads issued later
   // has to cover a path without them: rows before row 0 have negative
-  // offsets, which the buffer range check reads as zero, and lanes past the
-  // last band read rows of the last band, then leave.
+  // offsets, which read as zero, and lanes past the last band read rows of
+  // the last band, then leave.  The loads are issued in row order (kept by
+  // scheduling barriers), and dropped stores stand for the previous group's
+  // dx rows: the loop is then entered with the same accesses in flight, in
+  // the same order, as from its own back edge.
 #pragma unroll
   for (int q = 0; q < 3; ++q) halo[q] = IO::load(rx, off + (q - 3) * row_bytes);
 #pragma unroll
   for (int g = 0; g < kBwdGroup; ++g) {
+    __builtin_amdgcn_sched_barrier(0);
     xa[g] = IO::load(rx, off + g * row_bytes);
     da[g] = IO::load(rdy, off + g * row_bytes);
   }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int g = 0; g < kBwdGroup; ++g) IO::store(rdx, kNoRow + g * row_bytes, VT::zero());
 
   // Every thread stages its part of the SiLU' table (the mask builder's
   // barriers make it visible).
@@ -829,10 +884,7 @@ void bwd_main_kernel(BwdArgs a) {
   unpack_params<V>(praw, a.w_bf16, a.b_bf16, w, bv);
 
   Partials<Acc, V> acc;
-#pragma unroll
-  for (int k = 0; k < 5; ++k)
-#pragma unroll
-    for (int i = 0; i < V; ++i) acc.v[k][i] = (Acc)0, acc.run[k][i] = 0.0f;
+  acc.init();
 
   float h1[V], h2[V], h3[V], d1[V], d2[V], d3[V];
 #pragma unroll
@@ -861,15 +913,17 @@ void bwd_main_kernel(BwdArgs a) {
   // computed, and a group's dx rows are stored together after its last row
   // (loads and stores share one wait counter on this architecture).  Row
   // t0+idx emits dx of row t0+idx-3, so the band's first three rows emit
-  // nothing and three look-ahead rows, loaded during the last group,
-  // finish the band.
-  auto load = [&](Raw (&xr)[kBwdGroup], Raw (&dr)[kBwdGroup], int32_t at, int nrows) {
+  // nothing and three look-ahead rows, loaded during the last pair, finish
+  // the band.
+  //
+  // Rows 0..2 of a group load from `at`, rows 3.. from `at_rest`: `at`
+  // again for a whole group, kNoRow for the band's three look-ahead rows.
+  auto load = [&](Raw (&xr)[kBwdGroup], Raw (&dr)[kBwdGroup], int32_t at, int32_t at_rest) {
 #pragma unroll
     for (int g = 0; g < kBwdGroup; ++g) {
-      if (g < nrows) {
-        xr[g] = IO::load(rx, at + g * row_bytes);
-        dr[g] = IO::load(rdy, at + g * row_bytes);
-      }
+      const int32_t o = (g < 3 ? at : at_rest) + g * row_bytes;
+      xr[g] = IO::load(rx, o);
+      dr[g] = IO::load(rdy, o);
     }
   };
   auto run = [&](const Raw (&xr)[kBwdGroup], const Raw (&dr)[kBwdGroup], int32_t done, int nrows,
@@ -894,6 +948,11 @@ void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
       for (int g = 0; g < kBwdGroup; ++g) {
         if (g >= nrows) break;
+        // One row at a time (a scheduling barrier per row): interleaved,
+        // the rows' resets and masks need more registers than the kernel
+        // has, and the compiler then parks loads still in flight, which
+        // waits for them.
+        __builtin_amdgcn_sched_barrier(0);
         const uint32_t start = (starts >> g) & 1u;
         if (start) {
 #pragma unroll
@@ -908,19 +967,27 @@ void bwd_main_kernel(BwdArgs a) {
                                                   dxr[g]);
       }
     }
-    // dxr[g] holds the packed dx of row r+g-3.
+    // dxr[g] holds the packed dx of row r+g-3; the band's first three rows
+    // have no dx to store (kNoRow).
 #pragma unroll
     for (int g = 0; g < kBwdGroup; ++g)
-      if (g < nrows && done + g >= 3) IO::store(rdx, off + (g - 3) * row_bytes, dxr[g]);
-    if (accumulate) fold_partials(acc);
+      if (g < nrows)
+        IO::store(rdx, done + g >= 3 ? off + (g - 3) * row_bytes : kNoRow, dxr[g]);
+    if (accumulate) acc.fold();
     r += nrows;
     off += nrows * row_bytes;
   };
-  // T is a multiple of 2G (host rule).
+  // T is a multiple of 2G (host rule).  In the last pair the reload of the
+  // first buffer takes the look-ahead rows.  Under "bf16" the loop paces
+  // itself once per pair (see wait_vm); under "fp32", with more arithmetic
+  // per row, the wait costs more than it saves (about 3%), so there is none.
   for (int32_t done = 0; done < a.rows; done += 2 * kBwdGroup) {
-    load(xb, db, off + kBwdGroup * row_bytes, kBwdGroup);
+    const int32_t nb = off + kBwdGroup * row_bytes;
+    load(xb, db, nb, nb);
     run(xa, da, done, kBwdGroup, true);
-    load(xa, da, off + kBwdGroup * row_bytes, done + 2 * kBwdGroup < a.rows ? kBwdGroup : 3);
+    const int32_t na = off + kBwdGroup * row_bytes;
+    load(xa, da, na, done + 2 * kBwdGroup < a.rows ? na : kNoRow);
+    if (kBf16Policy) wait_vm<2 * kBwdGroup>();  // pace: only the reload remains in flight
     run(xb, db, done + kBwdGroup, kBwdGroup, true);
   }
   run(xa, da, a.rows, 3, false);
@@ -931,7 +998,7 @@ void bwd_main_kernel(BwdArgs a) {
   for (int k = 0; k < 5; ++k) {
     Acc* dst = part + (int64_t)k * a.C;
 #pragma unroll
-    for (int i = 0; i < V; ++i) dst[i] = acc.v[k][i];
+    for (int i = 0; i < V; ++i) dst[i] = acc.total(k, i);
   }
 }
 
