@@ -6,7 +6,6 @@ gcc into a temporary directory and run against ``oracle_pins``.  The real
 oracle is never modified.  Mutants only ever read inside their arrays.
 """
 import os
-import tempfile
 
 import pytest
 

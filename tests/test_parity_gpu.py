@@ -9,7 +9,6 @@ import numpy as np
 import pytest
 
 import gpu_cases as G
-from varlen_depthwise_causal_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 

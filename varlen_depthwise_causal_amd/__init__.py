@@ -17,6 +17,7 @@ import ctypes
 from ._lib import (  # noqa: F401
     VDC_BF16,
     VDC_BWD,
+    VDC_ENOBIAS,
     VDC_F32,
     VDC_FWD,
     VDC_SILU_GRAD_BF16,
@@ -171,7 +172,7 @@ def conv1d_bwd(x, weight, cu_seqlens, dy, *, bias=None, silu_grad_preactivation=
     dw_code = _dtype_code(dweight, "dweight")
     db_code = 0
     if dbias is not None and bias is None:
-        raise VdcError(5, "conv1d_bwd")
+        raise VdcError(VDC_ENOBIAS, "conv1d_bwd")
     if bias is not None:
         if dbias is None:
             dbias = torch.empty((C,), dtype=bias.dtype, device=dev)

@@ -10,8 +10,10 @@ from ._build import LIBRARY
 VDC_F32, VDC_BF16 = 0, 1
 VDC_SILU_GRAD_BF16, VDC_SILU_GRAD_FP32 = 0, 1
 VDC_FWD, VDC_BWD = 0, 1
-STATUS = {0: "VDC_OK", 1: "VDC_EINVAL", 2: "VDC_EDTYPE", 3: "VDC_EALIGN",
-          4: "VDC_EWORKSPACE", 5: "VDC_ENOBIAS", 6: "VDC_EHIP"}
+VDC_OK, VDC_EINVAL, VDC_EDTYPE, VDC_EALIGN, VDC_EWORKSPACE, VDC_ENOBIAS, VDC_EHIP = range(7)
+STATUS = {VDC_OK: "VDC_OK", VDC_EINVAL: "VDC_EINVAL", VDC_EDTYPE: "VDC_EDTYPE",
+          VDC_EALIGN: "VDC_EALIGN", VDC_EWORKSPACE: "VDC_EWORKSPACE",
+          VDC_ENOBIAS: "VDC_ENOBIAS", VDC_EHIP: "VDC_EHIP"}
 
 _lock = threading.Lock()
 _lib = None
