@@ -335,6 +335,13 @@ __device__ __forceinline__ void build_doc_mask(DocMask& m, uint32_t place, int32
   __syncthreads();
 }
 
+// True when `c` holds for no lane of the wave.  The row loops choose
+// between their plain and their masked path with it: a wave-uniform branch
+// runs one path, where a per-lane one would run both under lane masks and
+// keep every value of the first alive through the second (registers the
+// plain path needs).  Lanes without a start are correct on the masked path.
+__device__ __forceinline__ bool wave_none(bool c) { return __builtin_amdgcn_ballot_w64(c) == 0; }
+
 // Bit g set: row row_lo + j + g starts a document, for a row index j
 // relative to the workgroup's first row (1 <= n <= 32).
 __device__ __forceinline__ uint32_t doc_starts(const DocMask& m, int32_t j, int n) {
@@ -659,8 +666,8 @@ void fwd_kernel(FwdArgs a) {
   };
   auto compute = [&](const Raw (&buf)[kFwdGroup], Raw (&out)[kFwdGroup]) {
     const uint32_t starts = doc_starts(dmask, r, kFwdGroup);
-    if (starts == 0u) {
-      // No document starts in this group.
+    if (wave_none(starts != 0u)) {
+      // No document starts in this group, for any lane of the wave.
 #pragma unroll
       for (int g = 0; g < kFwdGroup; ++g) {
         float xc[V];
@@ -830,6 +837,8 @@ void bwd_main_kernel(BwdArgs a) {
   typedef typename VT::raw Raw;
   __shared__ __attribute__((aligned(16))) float lut_lds[kBf16Policy ? 2 * kLutN : 4];
   __shared__ DocMask dmask;
+  // Rows of a masked group, [row][thread]: x in words 0-1, dy in 2-3.
+  __shared__ u32x4 stage[kBwdGroup * kBlock];
   Lane L;
   const uint32_t place = block_place();
   if (place >= (uint32_t)a.blocks) return;  // padding workgroup: no lane
@@ -933,8 +942,9 @@ void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int g = 0; g < kBwdGroup; ++g) dxr[g] = VT::zero();
     const uint32_t starts = doc_starts(dmask, r, nrows);
-    if (hist == 0u && starts == 0u) {
-      // No document starts in rows r-2 .. r+nrows-1: no resets, no masks.
+    if (wave_none(hist != 0u || starts != 0u)) {
+      // No document starts in rows r-2 .. r+nrows-1, for any lane of the
+      // wave: no resets, no masks.
 #pragma unroll
       for (int g = 0; g < kBwdGroup; ++g) {
         if (g >= nrows) break;
@@ -945,14 +955,21 @@ void bwd_main_kernel(BwdArgs a) {
                                                    dxr[g]);
       }
     } else {
+      // A document start within reach: the group's rows go through this
+      // thread's LDS slots and a loop takes them in turn, each dx row back
+      // into its slot.  Unrolled like the plain path, this path needed more
+      // registers than the kernel has, and the allocation for it (parked
+      // values, register copies) slowed the plain path too.  Four rows per
+      // pass under "bf16" hide the table reads; under "fp32", with more
+      // registers per row, one.
+      u32x4* slot = stage + threadIdx.x;
 #pragma unroll
-      for (int g = 0; g < kBwdGroup; ++g) {
-        if (g >= nrows) break;
-        // One row at a time (a scheduling barrier per row): interleaved,
-        // the rows' resets and masks need more registers than the kernel
-        // has, and the compiler then parks loads still in flight, which
-        // waits for them.
-        __builtin_amdgcn_sched_barrier(0);
+      for (int g = 0; g < kBwdGroup; ++g)
+        if (g < nrows) slot[g * kBlock] = (u32x4){xr[g].x, xr[g].y, dr[g].x, dr[g].y};
+      constexpr int kMaskedUnroll = kBf16Policy ? 4 : 1;
+#pragma unroll kMaskedUnroll
+      for (int g = 0; g < nrows; ++g) {
+        const u32x4 row = slot[g * kBlock];
         const uint32_t start = (starts >> g) & 1u;
         if (start) {
 #pragma unroll
@@ -961,11 +978,19 @@ void bwd_main_kernel(BwdArgs a) {
         const uint32_t h3bits = (hist << 1) | start;
         hist = h3bits & 3u;
         float xc[V];
-        unpack<V>(xr[g], xc);
-        bwd_row<kBias, kBf16Policy, true, Acc, V>(w, bv, lut_lds, xc, dr[g], h1, h2, h3, d1, d2,
-                                                  d3, acc, accumulate, done + g >= 3, h3bits,
-                                                  dxr[g]);
+        unpack<V>((Raw){row.x, row.y}, xc);
+        Raw dxg = VT::zero();
+        bwd_row<kBias, kBf16Policy, true, Acc, V>(w, bv, lut_lds, xc, (Raw){row.z, row.w}, h1,
+                                                  h2, h3, d1, d2, d3, acc, accumulate,
+                                                  done + g >= 3, h3bits, dxg);
+        slot[g * kBlock] = (u32x4){dxg.x, dxg.y, 0u, 0u};
       }
+#pragma unroll
+      for (int g = 0; g < kBwdGroup; ++g)
+        if (g < nrows) {
+          const u32x4 v = slot[g * kBlock];
+          dxr[g] = (Raw){v.x, v.y};
+        }
     }
     // dxr[g] holds the packed dx of row r+g-3; the band's first three rows
     // have no dx to store (kNoRow).
