@@ -2,17 +2,20 @@
 conv1d + SiLU (forward kernel, then the backward main + reduce kernels) on
 the headline workload (S = 65536 tokens, C = 4096 channels, 22 lognormal
 documents, FP32 weight and bias, "bf16" SiLU' policy), inputs resident in
-HBM, timed with HIP events on the stream the library launches on.
+HBM.
 
 Prints one JSON line.  `value` is the step's algorithmic HBM traffic
 (forward 4 B + backward 6 B per token-channel, plus parameters) divided by
-the step time, in GB/s; per-direction GB/s, Mtokens/s and fractions of the
-8 TB/s MI355X HBM peak are alongside.  `roofline` prices one conv1d_bwd call
-(the main kernel and the small fixed-order reduce it enqueues) and
-`roofline_fwd` the forward kernel: algorithmic bytes over the mean
-event-timed launch, and, when profiles/headline_counters.md was taken on
-these same kernel sources, the HBM traffic the rocprofv3 counters saw per
-launch at the same duration.  `cpu_baseline` times the FP64 CPU oracle on a
+the step time: the wall clock of the timed steps, which run back to back
+with no instrumentation between them, bracketed by device synchronizations.
+Per-direction GB/s, Mtokens/s and fractions of the 8 TB/s MI355X HBM peak
+are alongside.  `roofline` prices one conv1d_bwd call (the main kernel and
+the small fixed-order reduce it enqueues) and `roofline_fwd` the forward
+kernel: algorithmic bytes over the mean launch duration, timed with one
+pair of HIP events on the launch stream around as many back-to-back calls
+as there are timed steps, and, when profiles/headline_counters.md was taken
+on these same kernel sources, the HBM traffic the rocprofv3 counters saw
+per launch at the same duration.  `cpu_baseline` times the FP64 CPU oracle on a
 bounded sample of the same workload on this host.
 
 `--copy-calibration` instead times a plain device copy of one [S, C] BF16
@@ -134,30 +137,39 @@ def gpu_leg(wl, policy, steps, warmup):
     db = torch.empty((wl.C,), dtype=torch.float32, device=dev) if b is not None else None
     ws = torch.empty(max(vdc.workspace_bytes("bwd", wl.S, wl.C), 1), dtype=torch.uint8, device=dev)
 
-    def step(ev=None):
-        if ev:
-            ev[0].record()
+    def fwd():
         vdc.conv1d_fwd(x, w, cu, bias=b, out=y)
-        if ev:
-            ev[1].record()
+
+    def bwd():
         vdc.conv1d_bwd(x, w, cu, dy, bias=b, silu_grad_preactivation=policy, workspace=ws,
                        dx=dx, dweight=dw, dbias=db)
-        if ev:
-            ev[2].record()
 
     for _ in range(warmup):
-        step()
+        fwd()
+        bwd()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
+    # The timed steps carry no instrumentation: an event recorded between
+    # two launches holds the next one back by several microseconds.
     t0 = time.perf_counter()
-    for i in range(steps):
-        step(events[i])
+    for _ in range(steps):
+        fwd()
+        bwd()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_ms = [e[0].elapsed_time(e[1]) for e in events]
-    bwd_ms = [e[1].elapsed_time(e[2]) for e in events]
-    return {"wall_s": wall, "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+
+    def per_launch_ms(call):
+        """Mean duration of one call over `steps` back-to-back calls, from
+        one pair of HIP events on the launch stream."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    return {"wall_s": wall, "fwd_ms": per_launch_ms(fwd), "bwd_ms": per_launch_ms(bwd),
             "plan_fwd": vdc.conv1d_plan("fwd", wl.S, wl.C, policy),
             "plan_bwd": vdc.conv1d_plan("bwd", wl.S, wl.C, policy)}
 
@@ -211,10 +223,6 @@ def main():
 
     traffic = counted_traffic(args.policy)
 
-    def pct(xs):
-        q = statistics.quantiles(xs, n=10) if len(xs) > 1 else [xs[0]] * 9
-        return [round(q[0], 4), round(q[-1], 4)]
-
     def roofline(kernel, alg_bytes, ms, counted, names):
         achieved = alg_bytes / (ms * 1e-3) / 1e9
         out = {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 2),
@@ -227,8 +235,8 @@ def main():
             out["traffic_over_algorithmic"] = round(nbytes / alg_bytes, 4)
         return out
 
-    fwd_ms = statistics.mean(g["fwd_ms"])
-    bwd_ms = statistics.mean(g["bwd_ms"])
+    fwd_ms = g["fwd_ms"]
+    bwd_ms = g["bwd_ms"]
     step_ms = g["wall_s"] * 1e3 / args.steps
     fb, bb = algorithmic_bytes(wl, "fwd"), algorithmic_bytes(wl, "bwd")
     fwd_gbs = fb / (fwd_ms * 1e-3) / 1e9
@@ -255,13 +263,11 @@ def main():
                    "S": wl.S, "C": wl.C, "docs": wl.num_docs, "policy": args.policy},
         "step_frac_of_hbm_peak": round(step_gbs / HBM_PEAK_GBS, 4),
         "step_mtokens_per_s": round(wl.S / (step_ms * 1e-3) / 1e6, 3),
-        "fwd": {"ms": round(fwd_ms, 4), "ms_median": round(statistics.median(g["fwd_ms"]), 4),
-                "ms_p10_p90": pct(g["fwd_ms"]),
+        "fwd": {"ms": round(fwd_ms, 4),
                 "GB_s": round(fwd_gbs, 2), "frac_of_peak": round(fwd_gbs / HBM_PEAK_GBS, 4),
                 "mtokens_per_s": round(wl.S / (fwd_ms * 1e-3) / 1e6, 3),
                 "algorithmic_bytes": fb, "plan": g["plan_fwd"]},
-        "bwd": {"ms": round(bwd_ms, 4), "ms_median": round(statistics.median(g["bwd_ms"]), 4),
-                "ms_p10_p90": pct(g["bwd_ms"]),
+        "bwd": {"ms": round(bwd_ms, 4),
                 "GB_s": round(bwd_gbs, 2), "frac_of_peak": round(bwd_gbs / HBM_PEAK_GBS, 4),
                 "mtokens_per_s": round(wl.S / (bwd_ms * 1e-3) / 1e6, 3),
                 "algorithmic_bytes": bb, "plan": g["plan_bwd"],
