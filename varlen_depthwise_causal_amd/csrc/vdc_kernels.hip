@@ -16,15 +16,17 @@
 //    C/4 is not a multiple of 64, simply continue into the next band.
 //  * The kernels run one wave per SIMD and the host picks T so that all
 //    waves fit the machine at once; each wave double-buffers groups of
-//    rows in registers and stores a group's outputs after its last row.
+//    rows in registers, stores a group's outputs after its last row, and
+//    paces itself once per pair of groups (wait_vm).
 //  * A lane keeps the previous three rows of x in registers; at a document
 //    start the window is cleared, which is exactly the zero history the
 //    forward prescribes, so no tap needs a mask.  Each workgroup marks the
-//    document starts of its rows in an LDS bitmask; groups of rows with no
-//    start nearby take a branch without any check.
+//    document starts of its rows in an LDS bitmask; a wave whose lanes have
+//    no start near a group takes a plain path without any check.
 //  * Tensors are addressed through buffer resources based at the wave's
-//    first row, with 32-bit per-lane offsets: rows outside [0, S) read as
-//    zero and their stores are dropped by the hardware range check.
+//    first row, with 32-bit per-lane offsets: rows outside [0, S) and
+//    negative offsets read as zero and their stores are dropped by the
+//    hardware range check.
 //  * Arithmetic is FP32 with one fixed evaluation order for the
 //    preactivation, shared by the forward and the backward recompute, so
 //    both see the same bits of p.
