@@ -40,6 +40,9 @@ SMALL = [
     ("c64_empty_ends", 10, 500, 64, [0, 0, 250, 0, 250, 0, 0], "bf16", None, None),
     ("c4096_rows", 11, 700, 4096, [350, 350], "f32", "f32", None),
     ("c520_deep", 12, 1200, 520, [1200], "f32", "f32", (0.05, 60.0)),
+    # one wave per band row (C/4 = 64) and a start every ~13 rows: nearly
+    # every group of every wave takes the masked path
+    ("c256_dense", 13, 2000, 256, "randint", "f32", "f32", None),
 ]
 
 
