@@ -109,7 +109,6 @@ def test_bitwise_across_workspaces_and_streams(torch_cuda):
     wl = _small(13, 20000, 520, "randint", "f32", "f32", (0.01, 60.0))
     dev = G.to_device(wl)
     need = vdc.workspace_bytes("bwd", wl.S, wl.C)
-    outs = []
     for policy in ("bf16", "fp32"):
         runs = []
         for i in range(3):
@@ -123,7 +122,6 @@ def test_bitwise_across_workspaces_and_streams(torch_cuda):
         for r in runs[1:]:
             for a, b in zip(runs[0], r):
                 assert torch.equal(a, b), policy
-        outs.append(runs[0])
 
 
 def test_empty_documents_change_nothing(torch_cuda):
