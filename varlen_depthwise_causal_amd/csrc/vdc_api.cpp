@@ -57,10 +57,10 @@ bool block_fits(int64_t nvec, int64_t rows) {
   return block_span_rows(nvec, rows) < 32 * (int64_t)(kDocMaskWords - 1);
 }
 
-// Tokens per band T.  Every band is one wave's work (64 lanes of C/V
-// channels each), and the kernels are built to run one wave per SIMD with a
-// deep load pipeline, so T is the smallest multiple of 2G for which the
-// bands fit one wave per SIMD of the MI355X (256 CUs x 4 SIMDs): all waves
+// Tokens per band T.  A band is covered by C/V lanes (V channels each), and
+// the kernels are built to run one wave per SIMD with a deep load pipeline,
+// so T is the smallest multiple of 2G for which all bands x C/V lanes fit
+// one wave per SIMD of the MI355X (256 CUs x 4 SIMDs x 64 lanes): all waves
 // start together and finish together.  Lowered if one wave's span of rows
 // would not fit 32-bit offsets (C in the hundreds of thousands) or one
 // workgroup's rows would not fit its document-start bitmask (small C with
@@ -77,12 +77,6 @@ int64_t pick_rows(int dir, int64_t S, int64_t C) {
   while (rows > step && (wave_span_rows(nvec, rows) * C * 2 >= (int64_t(1) << 31) ||
                          !block_fits(nvec, rows)))
     rows -= step;
-#ifdef VDC_ROWS_FORCE_FWD
-  if (dir == VDC_FWD) rows = VDC_ROWS_FORCE_FWD;
-#endif
-#ifdef VDC_ROWS_FORCE_BWD
-  if (dir == VDC_BWD) rows = VDC_ROWS_FORCE_BWD;
-#endif
   return rows;
 }
 
