@@ -43,6 +43,11 @@ SMALL = [
     # one wave per band row (C/4 = 64) and a start every ~13 rows: nearly
     # every group of every wave takes the masked path
     ("c256_dense", 13, 2000, 256, "randint", "f32", "f32", None),
+    # fewer tokens than the halo and than one row group: every band's tail,
+    # the look-ahead rows and the skipped first dx rows fall outside [0, S)
+    ("s1_c8", 15, 1, 8, [1], "f32", "f32", None),
+    ("s2_c64", 16, 2, 64, [0, 1, 1], "bf16", "f32", None),
+    ("s5_c136", 17, 5, 136, [2, 0, 3], "f32", None, None),
 ]
 
 
