@@ -174,6 +174,17 @@ def gpu_leg(wl, policy, steps, warmup):
             "plan_bwd": vdc.conv1d_plan("bwd", wl.S, wl.C, policy)}
 
 
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_leg(wl, policy):
     """The FP64 oracle, single-threaded, on every token of a channel sample."""
     import numpy as np
@@ -190,6 +201,7 @@ def cpu_leg(wl, policy):
     dt = time.perf_counter() - t0
     elems = wl.S * len(cols)
     return {"value": round(10 * elems / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "host_cpu": host_cpu_model(), "host_cpus": os.cpu_count(),
             "sample": "all %d tokens x %d of %d channels (channels are independent), "
                       "forward + backward, FP64 C oracle, one thread, %.1f s"
                       % (wl.S, len(cols), wl.C, dt),
