@@ -747,7 +747,6 @@ struct Partials {
   __device__ __forceinline__ Acc total(int k, int i) const { return v[k][i]; }
 };
 
-
 // dpre = dy * SiLU'(z) for the lane's V channels of one row.
 template <bool kBf16Policy, int V>
 __device__ __forceinline__ void dpre_row(const float (&p)[V], const float (&dyv)[V],
