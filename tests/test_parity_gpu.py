@@ -54,6 +54,34 @@ SMALL = [
 _small = G.small_case
 
 
+def _random_shapes(n, seed=2024):
+    """Seeded shapes: C any multiple of 8 up to 1032 (waves straddle bands at
+    many ratios), S from 1 to 3000, documents of random lengths with empty
+    and length-1 documents mixed in, bias or none, FP32 or BF16 parameters."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        C = 8 * int(rng.integers(1, 130))
+        S = int(rng.integers(1, 3001))
+        lengths, left = [], S
+        while left > 0:
+            kind = rng.random()
+            n_t = 0 if kind < 0.1 else (1 if kind < 0.2 else int(rng.integers(1, max(2, S // 3))))
+            n_t = min(n_t, left)
+            lengths.append(n_t)
+            left -= n_t
+        if rng.random() < 0.3:
+            lengths.append(0)
+        w_dt = "bf16" if rng.random() < 0.3 else "f32"
+        b_dt = None if rng.random() < 0.25 else ("bf16" if rng.random() < 0.3 else "f32")
+        sat = (0.02, 60.0) if rng.random() < 0.2 else None
+        out.append(("rand%02d_s%d_c%d" % (i, S, C), 100 + i, S, C, lengths, w_dt, b_dt, sat))
+    return out
+
+
+RANDOM = _random_shapes(48)
+
+
 @pytest.mark.parametrize("policy", ["bf16", "fp32"])
 @pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
 def test_small_all_elements(torch_cuda, case, policy):
@@ -67,6 +95,17 @@ def test_small_all_elements(torch_cuda, case, policy):
 
 FULL = [("uniform", "bf16"), ("headline", "bf16"), ("long", "fp32"),
         ("stress", "bf16"), ("stress", "fp32")]
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
+def test_random_shapes_all_elements(torch_cuda, case):
+    label = case[0]
+    policy = "fp32" if case[1] % 2 else "bf16"
+    G.say("CASE", label, policy)
+    wl = _small(*case[1:])
+    dev = G.to_device(wl)
+    y, dx, dw, db = G.run_gpu(dev, policy)
+    G.compare(wl, policy, y, dx, dw, db, label=label)
 
 
 @pytest.mark.parametrize("name,policy", FULL, ids=["%s-%s" % f for f in FULL])
