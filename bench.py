@@ -7,7 +7,8 @@ HBM.
 Prints one JSON line.  `value` is the step's algorithmic HBM traffic
 (forward 4 B + backward 6 B per token-channel, plus parameters) divided by
 the step time: the wall clock of the timed steps, which run back to back
-with no instrumentation between them, bracketed by device synchronizations.
+with no instrumentation between them, bracketed by device synchronizations
+(`ms_per_step_events` is the same region timed by one pair of HIP events).
 Per-direction GB/s, Mtokens/s and fractions of the 8 TB/s MI355X HBM peak
 are alongside.  `roofline` prices one conv1d_bwd call (the main kernel and
 the small fixed-order reduce it enqueues) and `roofline_fwd` the forward
@@ -148,14 +149,19 @@ def gpu_leg(wl, policy, steps, warmup):
         fwd()
         bwd()
     torch.cuda.synchronize()
-    # The timed steps carry no instrumentation: an event recorded between
-    # two launches holds the next one back by several microseconds.
+    # The timed steps carry no instrumentation between launches: an event
+    # recorded between two launches holds the next one back by several
+    # microseconds.  One event pair brackets the whole region.
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    s0.record()
     for _ in range(steps):
         fwd()
         bwd()
+    s1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    steps_event_ms = s0.elapsed_time(s1)
 
     def per_launch_ms(call):
         """Mean duration of one call over `steps` back-to-back calls, from
@@ -169,7 +175,8 @@ def gpu_leg(wl, policy, steps, warmup):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    return {"wall_s": wall, "fwd_ms": per_launch_ms(fwd), "bwd_ms": per_launch_ms(bwd),
+    return {"wall_s": wall, "steps_event_ms": steps_event_ms,
+            "fwd_ms": per_launch_ms(fwd), "bwd_ms": per_launch_ms(bwd),
             "plan_fwd": vdc.conv1d_plan("fwd", wl.S, wl.C, policy),
             "plan_bwd": vdc.conv1d_plan("bwd", wl.S, wl.C, policy)}
 
@@ -262,6 +269,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4),
+        "ms_per_step_events": round(g["steps_event_ms"] / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
