@@ -16,8 +16,9 @@
 //    C/4 is not a multiple of 64, simply continue into the next band.
 //  * The kernels run one wave per SIMD and the host picks T so that all
 //    waves fit the machine at once; each wave double-buffers groups of
-//    rows in registers, stores a group's outputs after its last row, and
-//    paces itself once per pair of groups (wait_vm).
+//    rows in registers and stores a group's outputs after its last row; the
+//    forward and the "bf16" backward pace themselves once per pair of
+//    groups (wait_vm).
 //  * A lane keeps the previous three rows of x in registers; at a document
 //    start the window is cleared, which is exactly the zero history the
 //    forward prescribes, so no tap needs a mask.  Each workgroup marks the
@@ -158,13 +159,13 @@ constexpr int32_t kNoRow = INT32_MIN;
 // (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt at their
 // maxima, so they are not waited for).
 //
-// The main loops use it to pace themselves: once per pair of row groups a
-// wave waits until everything but the next group's loads has retired,
-// stores included.  Without that wait each wave runs at its own pace, the
-// rows in flight across the machine drift apart, and the memory side loses
-// efficiency: at 8 KiB rows the L2's read latency to memory grows by about a
-// quarter, its DRAM credit stalls grow four- to fivefold, and the kernels
-// lose 5-11%.  Issuing the next group's loads before the stores of the
+// The forward and the "bf16" backward use it to pace themselves: once per
+// pair of row groups a wave waits until everything but the next group's
+// loads has retired, stores included.  Without that wait each wave runs at
+// its own pace, the rows in flight across the machine drift apart, and the
+// memory side loses efficiency: at 8 KiB rows the L2's read latency to
+// memory grows by about a quarter, its DRAM credit stalls grow four- to
+// fivefold, and the kernels lose 5-11%.  Issuing the next group's loads before the stores of the
 // group just computed (more accesses in flight per wave) is slower still.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -478,7 +479,6 @@ __device__ __forceinline__ void lut_stage_store(const LutStage& st, float* lds) 
   }
 }
 
-// Table index of BF16 bit pattern `bits` (16 bits, sign included).
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 // Byte offsets in the table of the two BF16 values packed in h (low half,
@@ -616,7 +616,7 @@ void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int q = 0; q < 3; ++q) halo[q] = VT::zero();
   off += 3 * row_bytes;
-  // Unconditional, so that no wait on the table or mask loads issued later
+  // Unconditional, so that no wait on the document-start loads issued later
   // has to cover a path without them: rows before row 0 have negative
   // offsets, which read as zero, and lanes past the last band read rows of
   // the last band, then leave.  The loads are issued in row order (kept by
