@@ -23,8 +23,11 @@ Readings (each one is also listed in the design notes):
           p64 +- dp rounds to ("bf16": the rounded argument may move)
     A_dpre = |dy| (D + A_g) + u |dpre|
     A_dx = sum_k |w_k| A_dpre[t+3-k] + 5 u sum_k |w_k dpre64[t+3-k]|
-  Where the four taps do not cancel, A is far below half an ulp and the
-  rule is the plain one-ulp rule.
+  Where nothing cancels, A is far below half an ulp and the rule is the
+  plain one-ulp rule.  Two things cancel.  The first is the taps of p or of
+  dx.  The second, under "fp32", is SiLU' near its zero, z ~ -1.278: there
+  s (1 + z (1 - s)) in binary32 has a large relative error, which A_g
+  covers.
 * rel-L2 = ||g - r||_2 / ||r||_2 over the entries compared, in FP64.  Under
   "bf16" the check is ||g - r|| <= bound ||r|| + ||F||, where F is the most
   the rare BF16 boundary flips of the preactivation (see bf16_flip) can move
