@@ -47,7 +47,9 @@
  *  - Work is only enqueued on `stream` (0 = the null stream).  Calls are
  *    safe to capture into a HIP graph once the workspace exists.
  *  - Every argument is validated on the host before anything is enqueued;
- *    on a non-zero status nothing was enqueued and no output was touched.
+ *    on any status but VDC_OK and VDC_EHIP nothing was enqueued and no
+ *    output was touched.  VDC_EHIP means the runtime refused a launch, and
+ *    an earlier launch of the same call may already be enqueued.
  *  - Two calls that may run concurrently need two workspaces.
  */
 #ifndef VDC_H
@@ -154,9 +156,10 @@ int conv1d_fwd(const void *x, const void *weight, int w_dtype,
  * the output dtype ([B] Description).  With more than 2048 partial rows
  * (long sequences of few channels) the reduce takes two launches: sums of
  * 2048-row ranges, then their sum, in an order that again depends on
- * (S, C) only.  S == 0 launches neither kernel: dweight
+ * (S, C) only.  S == 0 launches no main kernel ([B] Returns): dweight
  * (and dbias) are set to zero with hipMemsetAsync, or, if the stream is
- * being captured into a graph, with a small fill kernel ([B] Returns).
+ * being captured into a graph, by one launch of the reduce kernel over zero
+ * partial rows, so that the graph holds no memset node.
  * Returns a vdc_status.
  */
 int conv1d_bwd(const void *x, const void *weight, int w_dtype,
