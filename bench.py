@@ -19,8 +19,11 @@ on these same kernel sources, the HBM traffic the rocprofv3 counters saw
 per launch at the same duration.  `cpu_baseline` times the FP64 CPU oracle on a
 bounded sample of the same workload on this host.
 
-`--copy-calibration` instead times a plain device copy of one [S, C] BF16
-tensor: the reference kernel of known size that scales the byte counters.
+`--workload long` or `--workload stress` times another full-size workload
+in the same way (the headline is the default and the benchmark's line; the
+counted traffic is recorded for the headline only).  `--copy-calibration`
+instead times a plain device copy of one [S, C] BF16 tensor: the reference
+kernel of known size that scales the byte counters.
 """
 from __future__ import annotations
 
@@ -38,6 +41,12 @@ if ROOT not in sys.path:
 METRIC = "fwd/bwd HBM GB/s + Mtokens/s, S=64K C=4096 packed; % of HBM roofline"
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = "headline"
+# Workloads --workload accepts, with their document recipe.  Uniform is left
+# out: its 201 MB backward working set fits the 256 MB last-level cache, so
+# back-to-back steps on one buffer set would not measure HBM.
+DOCS = {"headline": "packed documents (lognormal lengths)",
+        "long": "one document",
+        "stress": "packed documents (lengths U{0..25}, empty ones included; 1% of x at +-60)"}
 CPU_SAMPLE_CHANNELS = 4096
 # HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
 # WRITE_SIZE, scaled by a plain copy's reading) for the kernels as built from
@@ -197,7 +206,7 @@ def cpu_leg(wl, policy):
     import numpy as np
     import oracle
 
-    cols = np.arange(CPU_SAMPLE_CHANNELS)
+    cols = np.arange(min(CPU_SAMPLE_CHANNELS, wl.C))
     x = oracle.decode_bf16(wl.x[:, cols])
     dy = oracle.decode_bf16(wl.dy[:, cols])
     w = oracle.decode_param(wl.w, wl.w_dtype)[cols]
@@ -223,7 +232,9 @@ def main():
     # training loop runs in.
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=200)
-    ap.add_argument("--policy", default="bf16", choices=["bf16", "fp32"])
+    ap.add_argument("--workload", default=WORKLOAD, choices=sorted(DOCS))
+    ap.add_argument("--policy", default=None, choices=["bf16", "fp32"],
+                    help="SiLU' policy (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain copy of one [S, C] BF16 tensor instead")
@@ -237,10 +248,12 @@ def main():
         return
 
     from varlen_depthwise_causal_amd import workloads as W
-    wl = W.make(WORKLOAD, workers=16)
+    if args.policy is None:
+        args.policy = W.SPECS[args.workload].policies[0]
+    wl = W.make(args.workload, workers=16)
     g = gpu_leg(wl, args.policy, args.steps, args.warmup)
 
-    traffic = counted_traffic(args.policy)
+    traffic = counted_traffic(args.policy) if args.workload == WORKLOAD else None
 
     def roofline(kernel, alg_bytes, ms, counted, names):
         achieved = alg_bytes / (ms * 1e-3) / 1e9
@@ -262,7 +275,8 @@ def main():
     bwd_gbs = bb / (bwd_ms * 1e-3) / 1e9
     step_gbs = (fb + bb) / (step_ms * 1e-3) / 1e9
     res = {
-        "metric": METRIC,
+        "metric": METRIC if args.workload == WORKLOAD else METRIC.replace(
+            "S=64K C=4096", "S=%dK C=%d" % (wl.S // 1024, wl.C)),
         "value": round(step_gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -276,10 +290,10 @@ def main():
         "dtype": "f32",
         "io_dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "%s: S=%d C=%d, %d packed documents (lognormal lengths), "
-                               "weight %s, bias %s, silu_grad_preactivation=%s"
-                               % (WORKLOAD, wl.S, wl.C, wl.num_docs, wl.w_dtype, wl.b_dtype,
-                                  args.policy),
+        "config": {"workload": "%s: S=%d C=%d, %d %s, weight %s, bias %s, "
+                               "silu_grad_preactivation=%s"
+                               % (args.workload, wl.S, wl.C, wl.num_docs, DOCS[args.workload],
+                                  wl.w_dtype, wl.b_dtype, args.policy),
                    "S": wl.S, "C": wl.C, "docs": wl.num_docs, "policy": args.policy},
         "step_frac_of_hbm_peak": round(step_gbs / HBM_PEAK_GBS, 4),
         "step_mtokens_per_s": round(wl.S / (step_ms * 1e-3) / 1e6, 3),
