@@ -97,6 +97,48 @@ FULL = [("uniform", "bf16"), ("headline", "bf16"), ("long", "fp32"),
         ("stress", "bf16"), ("stress", "fp32")]
 
 
+def _medium_shapes(n, seed=77):
+    """Seeded mid-size shapes (up to 6.4e7 elements) spread over the launch
+    planner: C any multiple of 8 up to 6400, S up to 250000, so band sizes,
+    band counts, straddling waves and padded grids vary.  Documents: one,
+    many short ones (U{0..30}), or random lengths up to S / 4."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        C = 8 * int(rng.integers(1, 801))
+        S = int(rng.integers(2000, max(2001, min(250000, 64_000_000 // C))))
+        kind = i % 3
+        if kind == 0:
+            lengths = [S]
+        else:
+            hi = 31 if kind == 1 else max(2, S // 4)
+            lengths, left = [], S
+            while left > 0:
+                n_t = min(int(rng.integers(0, hi)), left)
+                lengths.append(n_t)
+                left -= n_t
+        w_dt = "bf16" if rng.random() < 0.3 else "f32"
+        b_dt = None if rng.random() < 0.25 else ("bf16" if rng.random() < 0.3 else "f32")
+        out.append(("mid%02d_s%d_c%d" % (i, S, C), 300 + i, S, C, lengths, w_dt, b_dt, None))
+    return out
+
+
+MEDIUM = _medium_shapes(12)
+
+
+@pytest.mark.parametrize("case", MEDIUM, ids=[c[0] for c in MEDIUM])
+def test_medium_shapes_sampled(torch_cuda, case):
+    """Whole 8-channel groups of sampled columns, every token, both policies."""
+    label = case[0]
+    wl = _small(*case[1:])
+    dev = G.to_device(wl)
+    cols = G.sample_columns(wl.C, groups=8, seed=case[1])
+    for policy in ("bf16", "fp32"):
+        G.say("CASE", label, policy)
+        y, dx, dw, db = G.run_gpu(dev, policy)
+        G.compare(wl, policy, y, dx, dw, db, cols, label=label)
+
+
 @pytest.mark.parametrize("case", RANDOM, ids=[c[0] for c in RANDOM])
 def test_random_shapes_all_elements(torch_cuda, case):
     label = case[0]
