@@ -175,6 +175,38 @@ def test_plans_depend_on_shape_only(lib):
                 assert stage1 == 0
 
 
+def test_plan_invariants_over_random_shapes(lib):
+    """The planner's promises the kernels rely on, over seeded shapes from
+    S = 1 to 2^31 - 1 and C = 8 to 2^20: bands of a multiple of two row
+    groups covering S exactly once, lanes and workgroups that cover every
+    band, a wave's rows within 32-bit byte offsets, a workgroup's rows
+    within its document-start bitmask.  A shape may be refused (too many
+    lanes for 32-bit indices), never planned wrongly."""
+    import numpy as np
+    rng = np.random.default_rng(11)
+    planned = refused = 0
+    for _ in range(3000):
+        S = int(np.exp(rng.uniform(0.0, np.log(2.0 ** 31 - 1))))
+        C = 8 * int(np.exp(rng.uniform(0.0, np.log(2.0 ** 17))))
+        for d, group in ((FWD, 16), (BWD, 8)):
+            out = (ctypes.c_int64 * 10)()
+            rc = lib.conv1d_plan(d, S, C, 0, out)
+            if rc != OK:
+                assert rc == EINVAL
+                refused += 1
+                continue
+            planned += 1
+            rows, bands, lanes, blocks, threads, vec = out[0], out[1], out[2], out[3], out[4], out[8]
+            nvec = C // vec
+            assert rows % (2 * group) == 0 and rows >= 2 * group
+            assert bands * rows >= S and (bands - 1) * rows < S
+            assert lanes == bands * nvec and lanes < 2 ** 31
+            assert blocks == -(-lanes // threads)
+            assert (((-(-64 // nvec)) + 1) * rows + 8) * 2 * C < 2 ** 31
+            assert (-(-threads // nvec) + 1) * rows + 6 < 32 * 1023
+    assert planned > 5000 and refused < 1000
+
+
 def test_status_strings(lib):
     for s in range(7):
         assert len(lib.conv1d_status_string(s)) > 0
