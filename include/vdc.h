@@ -91,7 +91,8 @@ enum vdc_status {
     VDC_EALIGN = 3,     /* a tensor pointer is not aligned as required     */
     VDC_EWORKSPACE = 4, /* workspace missing or smaller than required      */
     VDC_ENOBIAS = 5,    /* dbias requested without a bias                  */
-    VDC_EHIP = 6        /* the HIP runtime refused a launch                */
+    VDC_EHIP = 6,       /* the HIP runtime refused a launch                */
+    VDC_ESCRATCH = 7    /* conv1d_bwd_noalloc: problem exceeds its scratch  */
 };
 
 /*
@@ -170,6 +171,47 @@ int conv1d_bwd(const void *x, const void *weight, int w_dtype,
                void *dbias, int db_dtype,
                void *workspace, size_t ws_bytes,
                hipStream_t stream);
+
+/*
+ * conv1d_bwd_noalloc - conv1d_bwd without a workspace argument, for callers
+ * that cannot allocate device memory: code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Arguments, validation, results and status codes are those of conv1d_bwd
+ * (the same kernels, launch plan and fixed reduction order, so the outputs
+ * are bitwise those of conv1d_bwd for the same inputs); the caller still
+ * owns and passes every input and output.  The workspace is instead a
+ * device array inside the library of conv1d_noalloc_scratch_bytes() bytes
+ * (16 MiB), one copy per GPU, held until the process ends.  The first call
+ * on a device looks up that device's copy (with hipGetSymbolAddress; the
+ * device of `stream` is made current for the lookup and restored after);
+ * no call allocates or frees anything.
+ *
+ * A problem whose workspace_bytes(VDC_BWD, S, C) exceeds the array returns
+ * VDC_ESCRATCH before anything is enqueued.  Every launch plan whose bands
+ * times C stays within 2^18 fits (at most one band per lane of a full
+ * machine: for example S = 65536 at C = 4096, S = 131072 at C = 8192,
+ * S = 262144 at C = 520, S = 16384 at C = 2048); plans for very long
+ * sequences, whose bands the planner shortens, and C in the hundreds of
+ * thousands may not (conv1d_plan and workspace_bytes tell in advance).
+ *
+ * All calls on one GPU share its array, and a call leaves its contents
+ * behind: two calls whose work may overlap in time on one GPU (on
+ * different streams, or captured into graphs replayed concurrently) race
+ * and give unspecified gradients.  Calls in one stream's order are safe.
+ * Nothing in the array needs to start at zero.
+ */
+int conv1d_bwd_noalloc(const void *x, const void *weight, int w_dtype,
+                       const void *bias, int b_dtype,
+                       const int32_t *cu_seqlens, int64_t num_docs,
+                       const void *dy, int64_t S, int64_t C, int policy,
+                       void *dx, void *dweight, int dw_dtype,
+                       void *dbias, int db_dtype,
+                       hipStream_t stream);
+
+/* conv1d_noalloc_scratch_bytes - size in bytes of the device array
+ * conv1d_bwd_noalloc uses as its workspace. */
+size_t conv1d_noalloc_scratch_bytes(void);
 
 /* conv1d_status_string - static English text of a vdc_status code. */
 const char *conv1d_status_string(int status);

@@ -12,7 +12,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "vdc.h")
 
-OK, EINVAL, EDTYPE, EALIGN, EWORKSPACE, ENOBIAS, EHIP = range(7)
+OK, EINVAL, EDTYPE, EALIGN, EWORKSPACE, ENOBIAS, EHIP, ESCRATCH = range(8)
 F32, BF16 = 0, 1
 FWD, BWD = 0, 1
 
@@ -207,8 +207,52 @@ def test_plan_invariants_over_random_shapes(lib):
     assert planned > 5000 and refused < 1000
 
 
+def bwd_noalloc(lib, x=A, w=W, wd=F32, b=BIAS, bd=F32, cu=CU, D=3, dy=DY, S=1000, C=64, pol=0,
+                dx=DX, dw=DW, dwd=F32, db=DB, dbd=F32):
+    return lib.conv1d_bwd_noalloc(x, w, wd, b, bd, cu, D, dy, S, C, pol, dx, dw, dwd, db, dbd, None)
+
+
+def test_noalloc_validation(lib):
+    """conv1d_bwd_noalloc refuses what conv1d_bwd refuses (no workspace to
+    check), and refuses problems larger than its array with VDC_ESCRATCH,
+    all before the HIP runtime is touched."""
+    n0 = lib.conv1d_launch_count()
+    assert bwd_noalloc(lib, C=20) == EINVAL
+    assert bwd_noalloc(lib, pol=2) == EDTYPE
+    assert bwd_noalloc(lib, wd=3) == EDTYPE
+    assert bwd_noalloc(lib, b=None) == ENOBIAS
+    assert bwd_noalloc(lib, dw=None) == EINVAL
+    assert bwd_noalloc(lib, dx=None) == EINVAL
+    assert bwd_noalloc(lib, dx=DX + 2) == EALIGN
+    assert bwd_noalloc(lib, dx=DY) == EINVAL
+    assert bwd_noalloc(lib, dw=DB) == EINVAL
+    # 2^24 tokens of 8 channels: 69906 partial rows, 22 MB of workspace
+    assert lib.workspace_bytes(BWD, 1 << 24, 8) > lib.conv1d_noalloc_scratch_bytes()
+    assert bwd_noalloc(lib, S=1 << 24, C=8) == ESCRATCH
+    assert bwd_noalloc(lib, S=1024, C=1 << 20) == ESCRATCH
+    assert lib.conv1d_launch_count() == n0
+
+
+def test_noalloc_scratch_covers_the_workloads(lib):
+    """The array (16 MiB) holds the workspace of every plan that keeps at
+    most one band per lane of a full machine (bands * C <= 2^18), among
+    them the five workloads' shapes."""
+    scratch = lib.conv1d_noalloc_scratch_bytes()
+    assert scratch == 16 << 20
+    for S, C in ((1000, 64), (16384, 2048), (65536, 4096), (131072, 8192), (262144, 520)):
+        assert 0 < lib.workspace_bytes(BWD, S, C) <= scratch
+    fits = 0
+    for C in (8, 64, 128, 136, 520, 1000, 4096, 8192, 65536):
+        for S in (1, 1000, 65536, 1 << 20, 1 << 24, 2 ** 31 - 1):
+            out = (ctypes.c_int64 * 10)()
+            if lib.conv1d_plan(BWD, S, C, 1, out) == OK and out[1] * C <= 1 << 18:
+                assert lib.workspace_bytes(BWD, S, C) <= scratch, (S, C)
+                fits += 1
+    assert fits > 30
+
+
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert len(lib.conv1d_status_string(s)) > 0
     assert lib.conv1d_status_string(99) == b"unknown status"
 

@@ -26,8 +26,8 @@ from ._lib import (  # noqa: F401
     load,
 )
 
-__all__ = ["conv1d_fwd", "conv1d_bwd", "workspace_bytes", "conv1d_plan",
-           "conv1d_launch_count", "VdcError"]
+__all__ = ["conv1d_fwd", "conv1d_bwd", "conv1d_bwd_noalloc", "workspace_bytes",
+           "noalloc_scratch_bytes", "conv1d_plan", "conv1d_launch_count", "VdcError"]
 
 _POLICIES = {"bf16": VDC_SILU_GRAD_BF16, "fp32": VDC_SILU_GRAD_FP32}
 
@@ -116,6 +116,11 @@ def conv1d_plan(direction: str, S: int, C: int, policy: str = "bf16") -> dict:
     return dict(zip(keys, (int(v) for v in out)))
 
 
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the device array conv1d_bwd_noalloc uses as its workspace."""
+    return int(load().conv1d_noalloc_scratch_bytes())
+
+
 def conv1d_launch_count() -> int:
     return int(load().conv1d_launch_count())
 
@@ -142,13 +147,10 @@ def conv1d_fwd(x, weight, cu_seqlens, *, bias=None, out=None, workspace=None):
     return out
 
 
-def conv1d_bwd(x, weight, cu_seqlens, dy, *, bias=None, silu_grad_preactivation="bf16",
-               workspace=None, dx=None, dweight=None, dbias=None):
-    """Returns (dx, dweight) or (dx, dweight, dbias) when a bias is given.
-
-    dweight / dbias default to the parameters' dtypes; pass preallocated
-    float32 buffers to receive FP32 gradients for BF16 parameters.
-    """
+def _bwd_outputs(x, weight, cu_seqlens, dy, bias, silu_grad_preactivation, dx, dweight, dbias,
+                 allocate):
+    """Checked arguments of a backward call; missing outputs are allocated
+    only when `allocate` (otherwise they are required)."""
     S, C, dev, w_code, b_code = _params(x, weight, cu_seqlens, bias)
     torch = _torch()
     if dy.dtype != torch.bfloat16 or dy.shape != x.shape:
@@ -157,6 +159,9 @@ def conv1d_bwd(x, weight, cu_seqlens, dy, *, bias=None, silu_grad_preactivation=
     if silu_grad_preactivation not in _POLICIES:
         raise ValueError("silu_grad_preactivation must be 'bf16' or 'fp32'")
     policy = _POLICIES[silu_grad_preactivation]
+    if not allocate and (dx is None or dweight is None or (bias is not None and dbias is None)):
+        raise ValueError("conv1d_bwd_noalloc allocates nothing: pass dx, dweight "
+                         "(and dbias with a bias)")
     if dx is None:
         dx = torch.empty_like(x)
     else:
@@ -181,6 +186,20 @@ def conv1d_bwd(x, weight, cu_seqlens, dy, *, bias=None, silu_grad_preactivation=
             if tuple(dbias.shape) != (C,):
                 raise ValueError("dbias must be [C]")
         db_code = _dtype_code(dbias, "dbias")
+    return S, C, dev, w_code, b_code, policy, dx, dweight, dw_code, dbias, db_code
+
+
+def conv1d_bwd(x, weight, cu_seqlens, dy, *, bias=None, silu_grad_preactivation="bf16",
+               workspace=None, dx=None, dweight=None, dbias=None):
+    """Returns (dx, dweight) or (dx, dweight, dbias) when a bias is given.
+
+    dweight / dbias default to the parameters' dtypes; pass preallocated
+    float32 buffers to receive FP32 gradients for BF16 parameters.
+    """
+    torch = _torch()
+    (S, C, dev, w_code, b_code, policy, dx, dweight, dw_code, dbias,
+     db_code) = _bwd_outputs(x, weight, cu_seqlens, dy, bias, silu_grad_preactivation, dx,
+                             dweight, dbias, allocate=True)
     need = workspace_bytes("bwd", S, C)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -193,4 +212,22 @@ def conv1d_bwd(x, weight, cu_seqlens, dy, *, bias=None, silu_grad_preactivation=
                            _ptr(workspace), ws_n, _stream(dev))
     if rc:
         raise VdcError(rc, "conv1d_bwd")
+    return (dx, dweight) if bias is None else (dx, dweight, dbias)
+
+
+def conv1d_bwd_noalloc(x, weight, cu_seqlens, dy, *, dx, dweight, bias=None, dbias=None,
+                       silu_grad_preactivation="bf16"):
+    """conv1d_bwd with the library's own device array as its workspace: no
+    allocation anywhere (the outputs are required).  Calls on one GPU share
+    the array, so calls that may overlap in time race.  Returns the same
+    tuple as conv1d_bwd."""
+    (S, C, dev, w_code, b_code, policy, dx, dweight, dw_code, dbias,
+     db_code) = _bwd_outputs(x, weight, cu_seqlens, dy, bias, silu_grad_preactivation, dx,
+                             dweight, dbias, allocate=False)
+    rc = load().conv1d_bwd_noalloc(_ptr(x), _ptr(weight), w_code, _ptr(bias), b_code,
+                                   _ptr(cu_seqlens), cu_seqlens.numel() - 1, _ptr(dy), S, C,
+                                   policy, _ptr(dx), _ptr(dweight), dw_code, _ptr(dbias),
+                                   db_code, _stream(dev))
+    if rc:
+        raise VdcError(rc, "conv1d_bwd_noalloc")
     return (dx, dweight) if bias is None else (dx, dweight, dbias)

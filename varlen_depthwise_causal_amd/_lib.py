@@ -10,10 +10,11 @@ from ._build import LIBRARY
 VDC_F32, VDC_BF16 = 0, 1
 VDC_SILU_GRAD_BF16, VDC_SILU_GRAD_FP32 = 0, 1
 VDC_FWD, VDC_BWD = 0, 1
-VDC_OK, VDC_EINVAL, VDC_EDTYPE, VDC_EALIGN, VDC_EWORKSPACE, VDC_ENOBIAS, VDC_EHIP = range(7)
+(VDC_OK, VDC_EINVAL, VDC_EDTYPE, VDC_EALIGN, VDC_EWORKSPACE, VDC_ENOBIAS, VDC_EHIP,
+ VDC_ESCRATCH) = range(8)
 STATUS = {VDC_OK: "VDC_OK", VDC_EINVAL: "VDC_EINVAL", VDC_EDTYPE: "VDC_EDTYPE",
           VDC_EALIGN: "VDC_EALIGN", VDC_EWORKSPACE: "VDC_EWORKSPACE",
-          VDC_ENOBIAS: "VDC_ENOBIAS", VDC_EHIP: "VDC_EHIP"}
+          VDC_ENOBIAS: "VDC_ENOBIAS", VDC_EHIP: "VDC_EHIP", VDC_ESCRATCH: "VDC_ESCRATCH"}
 
 _lock = threading.Lock()
 _lib = None
@@ -49,6 +50,11 @@ def load(path: str | None = None):
         lib.conv1d_bwd.argtypes = [vp, vp, i32, vp, i32, vp, i64, vp, i64, i64, i32,
                                    vp, vp, i32, vp, i32, vp, ctypes.c_size_t, vp]
         lib.conv1d_bwd.restype = i32
+        lib.conv1d_bwd_noalloc.argtypes = [vp, vp, i32, vp, i32, vp, i64, vp, i64, i64, i32,
+                                           vp, vp, i32, vp, i32, vp]
+        lib.conv1d_bwd_noalloc.restype = i32
+        lib.conv1d_noalloc_scratch_bytes.argtypes = []
+        lib.conv1d_noalloc_scratch_bytes.restype = ctypes.c_size_t
         lib.conv1d_status_string.argtypes = [i32]
         lib.conv1d_status_string.restype = ctypes.c_char_p
         lib.conv1d_plan.argtypes = [i32, i64, i64, i32, ctypes.POINTER(i64)]

@@ -191,109 +191,148 @@ extern "C" int conv1d_fwd(const void* x, const void* weight, int w_dtype, const 
   return launch_fwd(plan, a, bias != nullptr, stream) == hipSuccess ? VDC_OK : VDC_EHIP;
 }
 
-extern "C" int conv1d_bwd(const void* x, const void* weight, int w_dtype, const void* bias,
-                          int b_dtype, const int32_t* cu_seqlens, int64_t num_docs,
-                          const void* dy, int64_t S, int64_t C, int policy, void* dx,
-                          void* dweight, int dw_dtype, void* dbias, int db_dtype,
-                          void* workspace, size_t ws_bytes, hipStream_t stream) {
-  int rc = check_sizes(S, C, num_docs);
+namespace vdc {
+namespace {
+
+// The arguments of one backward call (conv1d_bwd and conv1d_bwd_noalloc
+// share their validation and their launches).
+struct BwdCall {
+  const void* x;
+  const void* weight;
+  int w_dtype;
+  const void* bias;
+  int b_dtype;
+  const int32_t* cu_seqlens;
+  int64_t num_docs;
+  const void* dy;
+  int64_t S;
+  int64_t C;
+  int policy;
+  void* dx;
+  void* dweight;
+  int dw_dtype;
+  void* dbias;
+  int db_dtype;
+};
+
+// Every check that does not involve the workspace.
+int bwd_check(const BwdCall& c) {
+  int rc = check_sizes(c.S, c.C, c.num_docs);
   if (rc) return rc;
-  if (!valid_dtype(w_dtype) || !valid_dtype(dw_dtype)) return VDC_EDTYPE;
-  if (bias && !valid_dtype(b_dtype)) return VDC_EDTYPE;
-  if (dbias && !valid_dtype(db_dtype)) return VDC_EDTYPE;
-  if (policy != VDC_SILU_GRAD_BF16 && policy != VDC_SILU_GRAD_FP32) return VDC_EDTYPE;
-  if (dbias && !bias) return VDC_ENOBIAS;
-  if (!dweight) return VDC_EINVAL;
-  if (!aligned(dweight, dtype_bytes(dw_dtype)) || (dbias && !aligned(dbias, dtype_bytes(db_dtype))))
+  if (!valid_dtype(c.w_dtype) || !valid_dtype(c.dw_dtype)) return VDC_EDTYPE;
+  if (c.bias && !valid_dtype(c.b_dtype)) return VDC_EDTYPE;
+  if (c.dbias && !valid_dtype(c.db_dtype)) return VDC_EDTYPE;
+  if (c.policy != VDC_SILU_GRAD_BF16 && c.policy != VDC_SILU_GRAD_FP32) return VDC_EDTYPE;
+  if (c.dbias && !c.bias) return VDC_ENOBIAS;
+  if (!c.dweight) return VDC_EINVAL;
+  if (!aligned(c.dweight, dtype_bytes(c.dw_dtype)) ||
+      (c.dbias && !aligned(c.dbias, dtype_bytes(c.db_dtype))))
     return VDC_EALIGN;
-  const size_t dw_n = (size_t)C * 4 * dtype_bytes(dw_dtype);
-  const size_t db_n = dbias ? (size_t)C * dtype_bytes(db_dtype) : 0;
-  if (overlaps(dweight, dw_n, dbias, db_n)) return VDC_EINVAL;
-
-  if (S == 0) {
-    // No token: dx is empty and both gradients are zero.  No main or
-    // reduce kernel runs; under graph capture the zeros come from the
-    // reduce kernel run over zero partial rows instead of a memset node.
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return VDC_EHIP;
-    if (cap == hipStreamCaptureStatusNone) {
-      if (hipMemsetAsync(dweight, 0, dw_n, stream) != hipSuccess) return VDC_EHIP;
-      if (dbias && hipMemsetAsync(dbias, 0, db_n, stream) != hipSuccess) return VDC_EHIP;
-      return VDC_OK;
-    }
-    Plan plan{};
-    plan.red_blocks = (int32_t)ceil_div(5 * C, kRedOut);
-    ReduceArgs r{};
-    r.part = nullptr;
-    r.dw = dweight;
-    r.db = dbias;
-    r.P = 0;
-    r.C = (int32_t)C;
-    r.dw_bf16 = dw_dtype == VDC_BF16;
-    r.db_bf16 = db_dtype == VDC_BF16;
-    g_launches.fetch_add(1, std::memory_order_relaxed);
-    return launch_bwd_reduce(plan, r, false, stream) == hipSuccess ? VDC_OK : VDC_EHIP;
-  }
-
-  if (!x || !weight || !cu_seqlens || !dy || !dx) return VDC_EINVAL;
-  if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16) || !aligned(weight, 16) ||
-      (bias && !aligned(bias, 16)))
+  const size_t dw_n = (size_t)c.C * 4 * dtype_bytes(c.dw_dtype);
+  const size_t db_n = c.dbias ? (size_t)c.C * dtype_bytes(c.db_dtype) : 0;
+  if (overlaps(c.dweight, dw_n, c.dbias, db_n)) return VDC_EINVAL;
+  if (c.S == 0) return VDC_OK;
+  if (!c.x || !c.weight || !c.cu_seqlens || !c.dy || !c.dx) return VDC_EINVAL;
+  if (!aligned(c.x, 16) || !aligned(c.dy, 16) || !aligned(c.dx, 16) || !aligned(c.weight, 16) ||
+      (c.bias && !aligned(c.bias, 16)))
     return VDC_EALIGN;
-  const size_t need = workspace_bytes(VDC_BWD, S, C);
-  if (!workspace || ws_bytes < need) return VDC_EWORKSPACE;
-  if (!aligned(workspace, 16)) return VDC_EALIGN;
-
-  const size_t act = (size_t)S * (size_t)C * 2;
-  const size_t w_n = (size_t)C * 4 * dtype_bytes(w_dtype);
-  const size_t b_n = bias ? (size_t)C * dtype_bytes(b_dtype) : 0;
-  const size_t cu_n = (size_t)(num_docs + 1) * 4;
-  const void* ins[5] = {x, dy, weight, bias, cu_seqlens};
+  const size_t act = (size_t)c.S * (size_t)c.C * 2;
+  const size_t w_n = (size_t)c.C * 4 * dtype_bytes(c.w_dtype);
+  const size_t b_n = c.bias ? (size_t)c.C * dtype_bytes(c.b_dtype) : 0;
+  const size_t cu_n = (size_t)(c.num_docs + 1) * 4;
+  const void* ins[5] = {c.x, c.dy, c.weight, c.bias, c.cu_seqlens};
   const size_t in_n[5] = {act, act, w_n, b_n, cu_n};
-  void* outs[4] = {dx, dweight, dbias, workspace};
-  const size_t out_n[4] = {act, dw_n, db_n, need};
-  for (int o = 0; o < 4; ++o) {
+  void* outs[3] = {c.dx, c.dweight, c.dbias};
+  const size_t out_n[3] = {act, dw_n, db_n};
+  for (int o = 0; o < 3; ++o) {
     for (int i = 0; i < 5; ++i)
       if (overlaps(outs[o], out_n[o], ins[i], in_n[i])) return VDC_EINVAL;
-    for (int q = o + 1; q < 4; ++q)
+    for (int q = o + 1; q < 3; ++q)
       if (overlaps(outs[o], out_n[o], outs[q], out_n[q])) return VDC_EINVAL;
   }
+  return plan_fits(make_plan(VDC_BWD, c.S, c.C, c.policy)) ? VDC_OK : VDC_EINVAL;
+}
 
-  const bool fp32_policy = policy == VDC_SILU_GRAD_FP32;
-  const Plan plan = make_plan(VDC_BWD, S, C, policy);
-  if (!plan_fits(plan)) return VDC_EINVAL;
+// The workspace must not overlap any tensor argument.
+bool workspace_overlaps(const BwdCall& c, const void* ws, size_t need) {
+  const size_t act = (size_t)c.S * (size_t)c.C * 2;
+  const void* p[8] = {c.x, c.dy, c.weight, c.bias, c.cu_seqlens, c.dx, c.dweight, c.dbias};
+  const size_t n[8] = {act, act, (size_t)c.C * 4 * dtype_bytes(c.w_dtype),
+                       c.bias ? (size_t)c.C * dtype_bytes(c.b_dtype) : 0,
+                       (size_t)(c.num_docs + 1) * 4, act,
+                       (size_t)c.C * 4 * dtype_bytes(c.dw_dtype),
+                       c.dbias ? (size_t)c.C * dtype_bytes(c.db_dtype) : 0};
+  for (int i = 0; i < 8; ++i)
+    if (overlaps(ws, need, p[i], n[i])) return true;
+  return false;
+}
+
+// S == 0: no token, dx is empty and both gradients are zero.  No main or
+// reduce kernel runs; under graph capture the zeros come from the reduce
+// kernel run over zero partial rows instead of a memset node.
+int bwd_zero(const BwdCall& c, hipStream_t stream) {
+  const size_t dw_n = (size_t)c.C * 4 * dtype_bytes(c.dw_dtype);
+  const size_t db_n = c.dbias ? (size_t)c.C * dtype_bytes(c.db_dtype) : 0;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess) return VDC_EHIP;
+  if (cap == hipStreamCaptureStatusNone) {
+    if (hipMemsetAsync(c.dweight, 0, dw_n, stream) != hipSuccess) return VDC_EHIP;
+    if (c.dbias && hipMemsetAsync(c.dbias, 0, db_n, stream) != hipSuccess) return VDC_EHIP;
+    return VDC_OK;
+  }
+  Plan plan{};
+  plan.red_blocks = (int32_t)ceil_div(5 * c.C, kRedOut);
+  ReduceArgs r{};
+  r.part = nullptr;
+  r.dw = c.dweight;
+  r.db = c.dbias;
+  r.P = 0;
+  r.C = (int32_t)c.C;
+  r.dw_bf16 = c.dw_dtype == VDC_BF16;
+  r.db_bf16 = c.db_dtype == VDC_BF16;
+  g_launches.fetch_add(1, std::memory_order_relaxed);
+  return launch_bwd_reduce(plan, r, false, stream) == hipSuccess ? VDC_OK : VDC_EHIP;
+}
+
+// The main kernel, then the fixed-order reduce, on a checked call (S > 0)
+// with a workspace of at least workspace_bytes(VDC_BWD, S, C) bytes.
+int bwd_enqueue(const BwdCall& c, void* workspace, hipStream_t stream) {
+  const bool fp32_policy = c.policy == VDC_SILU_GRAD_FP32;
+  const Plan plan = make_plan(VDC_BWD, c.S, c.C, c.policy);
   BwdArgs a{};
-  a.x = static_cast<const uint16_t*>(x);
-  a.dy = static_cast<const uint16_t*>(dy);
-  a.dx = static_cast<uint16_t*>(dx);
-  a.w = weight;
-  a.b = bias;
-  a.cu = cu_seqlens;
+  a.x = static_cast<const uint16_t*>(c.x);
+  a.dy = static_cast<const uint16_t*>(c.dy);
+  a.dx = static_cast<uint16_t*>(c.dx);
+  a.w = c.weight;
+  a.b = c.bias;
+  a.cu = c.cu_seqlens;
   a.part = workspace;
-  a.num_docs = (int32_t)num_docs;
-  a.w_bf16 = w_dtype == VDC_BF16;
-  a.b_bf16 = b_dtype == VDC_BF16;
-  a.S = (int32_t)S;
-  a.C = (int32_t)C;
-  a.nvec = (int32_t)(C / plan.vec);
+  a.num_docs = (int32_t)c.num_docs;
+  a.w_bf16 = c.w_dtype == VDC_BF16;
+  a.b_bf16 = c.b_dtype == VDC_BF16;
+  a.S = (int32_t)c.S;
+  a.C = (int32_t)c.C;
+  a.nvec = (int32_t)(c.C / plan.vec);
   a.rows = plan.rows;
   a.bands = plan.bands;
   a.blocks = plan.blocks;
   g_launches.fetch_add(1, std::memory_order_relaxed);
-  if (launch_bwd_main(plan, a, bias != nullptr, fp32_policy, stream) != hipSuccess) return VDC_EHIP;
+  if (launch_bwd_main(plan, a, c.bias != nullptr, fp32_policy, stream) != hipSuccess)
+    return VDC_EHIP;
 
   ReduceArgs r{};
   r.part = workspace;
-  r.dw = dweight;
-  r.db = dbias;
+  r.dw = c.dweight;
+  r.db = c.dbias;
   r.P = plan.bands;
-  r.C = (int32_t)C;
-  r.dw_bf16 = dw_dtype == VDC_BF16;
-  r.db_bf16 = db_dtype == VDC_BF16;
+  r.C = (int32_t)c.C;
+  r.dw_bf16 = c.dw_dtype == VDC_BF16;
+  r.db_bf16 = c.db_dtype == VDC_BF16;
   bool part_f64 = fp32_policy;
   if (plan.red_stage1 > 0) {
     // Many partial rows: sums of kRedBlockRows-row ranges first, into the
     // workspace after the largest partial-row area, then one pass over them.
-    r.inter = static_cast<char*>(workspace) + (size_t)plan.bands * 5 * (size_t)C * 8;
+    r.inter = static_cast<char*>(workspace) + (size_t)plan.bands * 5 * (size_t)c.C * 8;
     g_launches.fetch_add(1, std::memory_order_relaxed);
     if (launch_bwd_reduce_rows(plan, r, part_f64, stream) != hipSuccess) return VDC_EHIP;
     r.part = r.inter;
@@ -302,6 +341,49 @@ extern "C" int conv1d_bwd(const void* x, const void* weight, int w_dtype, const 
   }
   g_launches.fetch_add(1, std::memory_order_relaxed);
   return launch_bwd_reduce(plan, r, part_f64, stream) == hipSuccess ? VDC_OK : VDC_EHIP;
+}
+
+}  // namespace
+}  // namespace vdc
+
+extern "C" int conv1d_bwd(const void* x, const void* weight, int w_dtype, const void* bias,
+                          int b_dtype, const int32_t* cu_seqlens, int64_t num_docs,
+                          const void* dy, int64_t S, int64_t C, int policy, void* dx,
+                          void* dweight, int dw_dtype, void* dbias, int db_dtype,
+                          void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const BwdCall c{x, weight, w_dtype, bias, b_dtype, cu_seqlens, num_docs, dy, S, C, policy,
+                  dx, dweight, dw_dtype, dbias, db_dtype};
+  int rc = bwd_check(c);
+  if (rc) return rc;
+  if (S == 0) return bwd_zero(c, stream);
+  const size_t need = workspace_bytes(VDC_BWD, S, C);
+  if (!workspace || ws_bytes < need) return VDC_EWORKSPACE;
+  if (!aligned(workspace, 16)) return VDC_EALIGN;
+  if (workspace_overlaps(c, workspace, need)) return VDC_EINVAL;
+  return bwd_enqueue(c, workspace, stream);
+}
+
+extern "C" size_t conv1d_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" int conv1d_bwd_noalloc(const void* x, const void* weight, int w_dtype,
+                                  const void* bias, int b_dtype, const int32_t* cu_seqlens,
+                                  int64_t num_docs, const void* dy, int64_t S, int64_t C,
+                                  int policy, void* dx, void* dweight, int dw_dtype, void* dbias,
+                                  int db_dtype, hipStream_t stream) {
+  const BwdCall c{x, weight, w_dtype, bias, b_dtype, cu_seqlens, num_docs, dy, S, C, policy,
+                  dx, dweight, dw_dtype, dbias, db_dtype};
+  int rc = bwd_check(c);
+  if (rc) return rc;
+  if (S == 0) return bwd_zero(c, stream);
+  // The same workspace layout as conv1d_bwd, in the library's own device
+  // array: refused before anything is enqueued when it does not fit.
+  if (workspace_bytes(VDC_BWD, S, C) > kScratchBytes) return VDC_ESCRATCH;
+  // The stream's device holds the kernels' copy of the array.
+  int dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess) return VDC_EHIP;
+  void* scratch = nullptr;
+  if (scratch_pointer(dev, &scratch) != hipSuccess || !scratch) return VDC_EHIP;
+  return bwd_enqueue(c, scratch, stream);
 }
 
 extern "C" const char* conv1d_status_string(int status) {
@@ -313,6 +395,9 @@ extern "C" const char* conv1d_status_string(int status) {
     case VDC_EWORKSPACE: return "workspace missing or too small";
     case VDC_ENOBIAS: return "dbias requested without a bias";
     case VDC_EHIP: return "HIP runtime error";
+    case VDC_ESCRATCH:
+      return "the call needs more scratch than conv1d_bwd_noalloc holds "
+             "(see conv1d_noalloc_scratch_bytes); use conv1d_bwd with a workspace";
     default: return "unknown status";
   }
 }

@@ -117,6 +117,17 @@ struct ReduceArgs {
   int32_t db_bf16;
 };
 
+// Bytes of the library's own device array that conv1d_bwd_noalloc uses as
+// its workspace (one copy per GPU, held until the process ends).  Every
+// backward whose launch plan keeps at most one band per lane of a full
+// machine (bands * C <= 2^18) needs at most 10.5 MB of partial rows; 16 MiB
+// covers those with the reduce's first-stage sums on top.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+
+// Device address of that array on `device` (looked up once per device,
+// with the device current, then cached).
+hipError_t scratch_pointer(int device, void** out);
+
 // Launchers (return the hipError_t of the launch).
 hipError_t launch_fwd(const Plan& plan, const FwdArgs& a, bool has_bias, hipStream_t s);
 hipError_t launch_bwd_main(const Plan& plan, const BwdArgs& a, bool has_bias, bool fp32_policy,

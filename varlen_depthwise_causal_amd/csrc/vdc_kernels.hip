@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <mutex>
 #include <stdint.h>
 
 #include "vdc_internal.h"
@@ -1138,6 +1139,47 @@ hipError_t launch_bwd_main_v(const Plan& plan, const BwdArgs& a, bool has_bias, 
 }
 
 }  // namespace
+
+// ======================================================== scratch array ==
+//
+// The workspace of conv1d_bwd_noalloc: a file-scope device array, one copy
+// per GPU.  In host code its name stands for a host-side shadow, not a
+// device address, so the kernels only ever receive the address that
+// hipGetSymbolAddress returns for the device.  The lookup is made once per
+// device, with that device current, and cached.  Calls on one GPU share
+// the array: two such calls that may overlap in time race.  Nothing in it
+// needs to start at zero (the backward writes every byte it reads).
+
+namespace {
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t scratch_pointer(int device, void** out) {
+  *out = nullptr;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    int current = 0;
+    hipError_t e = hipGetDevice(&current);
+    if (e != hipSuccess) return e;
+    if (current != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (current != device) {
+      const hipError_t r = hipSetDevice(current);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
+}
 
 // ============================================================ launchers ==
 
