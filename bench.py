@@ -17,7 +17,14 @@ pair of HIP events on the launch stream around as many back-to-back calls
 as there are timed steps, and, when profiles/headline_counters.md was taken
 on these same kernel sources, the HBM traffic the rocprofv3 counters saw
 per launch at the same duration.  `cpu_baseline` times the FP64 CPU oracle on a
-bounded sample of the same workload on this host.
+bounded sample of the same workload on this host, on one thread and
+(`all_cores`) over channel blocks on every core of this process.
+
+`--warmup` is a minimum: warm-up steps continue until launch times settle
+(the GPU's clocks ramp over its first ~100 launches), and the JSON records
+how many ran.  `workloads` adds per-call forward and backward GB/s of the
+other full-size workloads (Long, Stress under both policies, Uniform over
+rotated buffer sets) and of the headline under the "fp32" policy.
 
 `--workload long` or `--workload stress` times another full-size workload
 in the same way (the headline is the default and the benchmark's line; the
@@ -125,6 +132,43 @@ def copy_calibration(steps, warmup):
                                            "steps": steps}}), flush=True)
 
 
+# Warm-up floor.  The first ~100 launches after the GPU wakes run up to 40%
+# slower while its clocks settle, so --warmup is a minimum: warm-up steps
+# continue, in blocks of SETTLE_BLOCK, until at least SETTLE_MIN_STEPS steps
+# and SETTLE_MIN_S seconds have passed and the last three blocks' mean step
+# times agree within SETTLE_TOL, or until SETTLE_MAX_S seconds.
+SETTLE_BLOCK = 10
+SETTLE_MIN_STEPS = 100
+SETTLE_MIN_S = 0.1
+SETTLE_TOL = 0.01
+SETTLE_MAX_S = 2.0
+
+
+def settle(step, min_steps):
+    """Run warm-up steps until launch times settle (see SETTLE_*); returns
+    the steps run, their wall time and the last blocks' step times."""
+    import torch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n, blocks = 0, []
+    while True:
+        e0.record()
+        for _ in range(SETTLE_BLOCK):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        n += SETTLE_BLOCK
+        blocks.append(e0.elapsed_time(e1) / SETTLE_BLOCK)
+        el = time.perf_counter() - t0
+        last = blocks[-3:]
+        steady = len(last) == 3 and max(last) - min(last) <= SETTLE_TOL * min(last)
+        if (n >= max(min_steps, SETTLE_MIN_STEPS) and el >= SETTLE_MIN_S and steady) \
+                or el >= SETTLE_MAX_S:
+            return {"steps_run": n, "ms": round(el * 1e3, 1), "settled": steady,
+                    "last_block_ms_per_step": [round(b, 4) for b in last]}
+
+
 def gpu_leg(wl, policy, steps, warmup):
     import torch
     import varlen_depthwise_causal_amd as vdc
@@ -154,10 +198,7 @@ def gpu_leg(wl, policy, steps, warmup):
         vdc.conv1d_bwd(x, w, cu, dy, bias=b, silu_grad_preactivation=policy, workspace=ws,
                        dx=dx, dweight=dw, dbias=db)
 
-    for _ in range(warmup):
-        fwd()
-        bwd()
-    torch.cuda.synchronize()
+    warm = settle(lambda: (fwd(), bwd()), warmup)
     # The timed steps carry no instrumentation between launches: an event
     # recorded between two launches holds the next one back by several
     # microseconds.  One event pair brackets the whole region.
@@ -184,10 +225,109 @@ def gpu_leg(wl, policy, steps, warmup):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    return {"wall_s": wall, "steps_event_ms": steps_event_ms,
+    return {"wall_s": wall, "steps_event_ms": steps_event_ms, "warm": warm,
             "fwd_ms": per_launch_ms(fwd), "bwd_ms": per_launch_ms(bwd),
             "plan_fwd": vdc.conv1d_plan("fwd", wl.S, wl.C, policy),
             "plan_bwd": vdc.conv1d_plan("bwd", wl.S, wl.C, policy)}
+
+
+# Workloads timed beside the headline step (`workloads` key): (workload,
+# policy, rotated buffer sets).  Uniform's tensors fit the 256 MB last-level
+# cache, so its calls rotate over four sets of x, dy, y and dx (800 MB).
+EXTRA = (("headline", "fp32", 1), ("long", "fp32", 1), ("stress", "bf16", 1),
+         ("stress", "fp32", 1), ("uniform", "bf16", 4))
+EXTRA_CALLS = 50
+
+
+def launch_ms(wl, policies, calls, sets):
+    """Per-call duration (ms) of conv1d_fwd and of conv1d_bwd under each
+    policy: one pair of HIP events around `calls` back-to-back calls on the
+    launch stream, rotating over `sets` buffer sets, after a settling
+    warm-up."""
+    import numpy as np
+    import torch
+    import varlen_depthwise_causal_amd as vdc
+    dev = torch.device("cuda:0")
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    w = torch.from_numpy(wl.w).to(dev) if wl.w_dtype == "f32" else bf16(wl.w)
+    b = None
+    if wl.b is not None:
+        b = torch.from_numpy(wl.b).to(dev) if wl.b_dtype == "f32" else bf16(wl.b)
+    cu = torch.from_numpy(wl.cu).to(dev)
+    x0, dy0 = bf16(wl.x), bf16(wl.dy)
+    bufs = []
+    for i in range(sets):
+        x = x0 if i == 0 else x0.clone()
+        dy = dy0 if i == 0 else dy0.clone()
+        bufs.append((x, dy, torch.empty_like(x), torch.empty_like(x)))
+    dw = torch.empty((wl.C, 4), dtype=torch.float32, device=dev)
+    db = torch.empty((wl.C,), dtype=torch.float32, device=dev) if b is not None else None
+    ws = torch.empty(max(vdc.workspace_bytes("bwd", wl.S, wl.C), 1), dtype=torch.uint8,
+                     device=dev)
+
+    def fwd(i):
+        x, _, y, _ = bufs[i % sets]
+        vdc.conv1d_fwd(x, w, cu, bias=b, out=y)
+
+    def bwd(i, policy):
+        x, dy, _, dx = bufs[i % sets]
+        vdc.conv1d_bwd(x, w, cu, dy, bias=b, silu_grad_preactivation=policy, workspace=ws,
+                       dx=dx, dweight=dw, dbias=db)
+
+    def timed(call):
+        ctr = [0]
+
+        def step():
+            call(ctr[0])
+            ctr[0] += 1
+        settle(step, 0)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(calls):
+            call(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / calls
+
+    out = {"fwd": timed(fwd)}
+    for policy in policies:
+        out["bwd_" + policy] = timed(lambda i, p=policy: bwd(i, p))
+    del bufs, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def workloads_leg():
+    """Forward and backward GB/s of the other full-size workloads (and of the
+    headline under the "fp32" policy), each call timed on its own."""
+    from varlen_depthwise_causal_amd import workloads as W
+    by_wl = {}
+    for name, policy, sets in EXTRA:
+        by_wl.setdefault((name, sets), []).append(policy)
+    res = {}
+    for (name, sets), policies in by_wl.items():
+        wl = W.make(name, workers=16)
+        t = launch_ms(wl, policies, EXTRA_CALLS, sets)
+        fb, bb = algorithmic_bytes(wl, "fwd"), algorithmic_bytes(wl, "bwd")
+
+        def rate(nbytes, ms):
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            return {"ms": round(ms, 4), "GB_s": round(gbs, 1),
+                    "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                    "mtokens_per_s": round(wl.S / (ms * 1e-3) / 1e6, 2)}
+        for policy in policies:
+            key = "%s/%s" % (name, policy)
+            res[key] = {"S": wl.S, "C": wl.C, "docs": wl.num_docs,
+                        "buffer_sets": sets, "calls": EXTRA_CALLS,
+                        "fwd": rate(fb, t["fwd"]), "bwd": rate(bb, t["bwd_" + policy])}
+            print("workload %s: fwd %.4f ms, bwd %.4f ms" % (key, t["fwd"], t["bwd_" + policy]),
+                  file=sys.stderr, flush=True)
+        del wl
+    return res
 
 
 def host_cpu_model():
@@ -201,41 +341,76 @@ def host_cpu_model():
     return None
 
 
+# Host threads of the all-core oracle leg: the CPU share of a one-GPU machine
+# (whatever os.cpu_count() reports there).
+CPU_THREADS_MAX = 16
+
+
 def cpu_leg(wl, policy):
-    """The FP64 oracle, single-threaded, on every token of a channel sample."""
+    """The FP64 oracle on every token of a channel sample: one thread (the
+    baseline), then the same oracle code over channel blocks on all of this
+    process's cores (channels are independent)."""
     import numpy as np
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
 
     cols = np.arange(min(CPU_SAMPLE_CHANNELS, wl.C))
     x = oracle.decode_bf16(wl.x[:, cols])
     dy = oracle.decode_bf16(wl.dy[:, cols])
     w = oracle.decode_param(wl.w, wl.w_dtype)[cols]
     b = oracle.decode_param(wl.b, wl.b_dtype)[cols] if wl.b is not None else None
+
+    def run(xs, dys, ws, bs):
+        oracle.forward(xs, ws, bs, wl.cu, want=("y",))
+        oracle.backward(xs, ws, bs, wl.cu, dys, policy, want=("dx", "dw", "db"))
+
     t0 = time.perf_counter()
-    oracle.forward(x, w, b, wl.cu, want=("y",))
-    oracle.backward(x, w, b, wl.cu, dy, policy, want=("dx", "dw", "db"))
+    run(x, dy, w, b)
     dt = time.perf_counter() - t0
     elems = wl.S * len(cols)
-    return {"value": round(10 * elems / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "host_cpu": host_cpu_model(), "host_cpus": os.cpu_count(),
-            "sample": "all %d tokens x %d of %d channels (channels are independent), "
-                      "forward + backward, FP64 C oracle, one thread, %.1f s"
-                      % (wl.S, len(cols), wl.C, dt),
-            "mtokens_per_s_full_width": round(elems / wl.C / dt / 1e6, 5)}
+    res = {"value": round(10 * elems / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "host_cpu": host_cpu_model(), "host_cpus": os.cpu_count(),
+           "sample": "all %d tokens x %d of %d channels (channels are independent), "
+                     "forward + backward, FP64 C oracle, one thread, %.1f s"
+                     % (wl.S, len(cols), wl.C, dt),
+           "mtokens_per_s_full_width": round(elems / wl.C / dt / 1e6, 5)}
+    # All cores: the unchanged oracle on contiguous channel blocks, one per
+    # thread (its C code runs with the interpreter lock released).
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    n = max(1, min(n, CPU_THREADS_MAX))
+    parts = np.array_split(np.arange(len(cols)), n)
+    blocks = [(np.ascontiguousarray(x[:, p]), np.ascontiguousarray(dy[:, p]),
+               np.ascontiguousarray(w[p]), None if b is None else np.ascontiguousarray(b[p]))
+              for p in parts]
+    del x, dy
+    with ThreadPoolExecutor(n) as pool:
+        t0 = time.perf_counter()
+        list(pool.map(lambda blk: run(*blk), blocks))
+        dt_all = time.perf_counter() - t0
+    res["all_cores"] = {"value": round(10 * elems / dt_all / 1e9, 4), "unit": "GB/s",
+                        "cores": n, "kind": "oracle",
+                        "sample": "the same sample in %d channel blocks, one thread each, "
+                                  "%.2f s" % (n, dt_all),
+                        "mtokens_per_s_full_width": round(elems / wl.C / dt_all / 1e6, 5)}
+    return res
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # The first ~100 launches after the GPU wakes run up to 40% slower while
-    # clocks settle; 200 warm-up steps (~0.1 s) reach the steady state a
-    # training loop runs in.
+    # --warmup is a minimum: warm-up continues until launch times settle
+    # (settle()), so a small value still times the steady state.
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=WORKLOAD, choices=sorted(DOCS))
     ap.add_argument("--policy", default=None, choices=["bf16", "fp32"],
                     help="SiLU' policy (default: the workload's own)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other workloads' per-call timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="time a plain copy of one [S, C] BF16 tensor instead")
     args = ap.parse_args()
@@ -284,6 +459,9 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4),
         "ms_per_step_events": round(g["steps_event_ms"] / args.steps, 4),
+        "warmup_steps_run": g["warm"]["steps_run"],
+        "warmup_ms": g["warm"]["ms"],
+        "warmup_settled": g["warm"]["settled"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -312,6 +490,9 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_leg(wl, args.policy)
+    if not args.no_workloads and args.workload == WORKLOAD:
+        del wl
+        res["workloads"] = workloads_leg()
     print(json.dumps(res), flush=True)
 
 
