@@ -3,11 +3,11 @@ SiLU (documentation page CakeCausalConv1dFunction, class description).
 
 Only (x, weight, cu_seqlens, bias) are saved: the backward recomputes the
 preactivation from x inside the backward kernel, so no activation other than
-the inputs is kept alive between the passes.  The incoming gradient is
-materialized as a contiguous BF16 tensor when autograd hands over another
-dtype or layout, and the gradients of weight and bias come back in the
-parameters' dtypes.  Every step runs in libvdc.so's kernels through
-conv1d_fwd / conv1d_bwd.
+the inputs is kept alive between the passes.  The kernels read the output
+gradient as dense row-major BF16, so a gradient of any other dtype or
+strides is converted (a copy) before the call.  The weight and bias
+gradients are returned in the dtypes of the parameters they belong to.
+Every step runs in libvdc.so's kernels through conv1d_fwd / conv1d_bwd.
 """
 from __future__ import annotations
 

@@ -39,6 +39,7 @@
 #include <stdint.h>
 
 #include "vdc_internal.h"
+#include "vdc_search.h"
 
 namespace vdc {
 namespace {
@@ -263,21 +264,21 @@ __device__ __forceinline__ void unpack_params(const ParamRaw<V>& raw, int w_bf16
 
 // First index i in [0, n) with cu[i] >= v (n if none), by a whole wave:
 // each round probes 64 evenly spaced entries and keeps the bracket, so the
-// range shrinks 64-fold per dependent load.  Terminates for any contents.
+// range shrinks 64-fold per dependent load.  Terminates for any contents;
+// the bracket arithmetic is 64-bit (vdc_search.h), so every probe lies in
+// [0, n) up to n = 2^31 - 1.
 __device__ __forceinline__ int32_t wave_lower_bound(const int32_t* cu, int32_t n, int32_t v) {
-  const int32_t lane = threadIdx.x & 63;
-  int32_t lo = 0, hi = n;
+  const int lane = (int)(threadIdx.x & 63);
+  int64_t lo = 0, hi = n;
   while (lo < hi) {
-    const int32_t step = (hi - lo + 63) >> 6;
-    const int32_t idx = lo + lane * step;
-    const bool less = idx < hi && cu[idx] < v;
+    const int64_t step = search_step(lo, hi);
+    const int64_t idx = search_probe(lo, hi, step, lane);
+    const bool less = idx >= 0 && cu[idx] < v;
     const uint64_t ball = __ballot(less);
-    const int32_t c = ~ball == 0 ? 64 : (int32_t)__builtin_ctzll(~ball);
-    const int32_t nlo = c == 0 ? lo : lo + (c - 1) * step + 1;
-    hi = min(hi, lo + c * step);
-    lo = nlo;
+    const int c = ~ball == 0 ? 64 : (int)__builtin_ctzll(~ball);
+    search_narrow(lo, hi, step, c);
   }
-  return lo;
+  return (int32_t)lo;
 }
 
 struct DocMask {
