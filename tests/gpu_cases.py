@@ -85,42 +85,99 @@ def sample_columns(C, groups=8, seed=0):
     return np.concatenate([np.arange(8 * v, 8 * v + 8) for v in sorted(pick)])
 
 
-def compare(wl, policy, y, dx, dw, db, cols=None, *, label=""):
-    """Check GPU outputs (device tensors) on columns `cols` (all if None) against the oracle."""
-    torch = torch_mod()
-    if cols is None:
-        cols = np.arange(wl.C)
-    cols_t = torch.from_numpy(cols.astype(np.int64)).to(y.device)
-    y_h = oracle.decode_bf16(bf16_bits(y.index_select(1, cols_t)))
-    dx_h = oracle.decode_bf16(bf16_bits(dx.index_select(1, cols_t)))
-    dw_h = dw.float().cpu().numpy().astype(np.float64)[cols]
-    db_h = db.float().cpu().numpy().astype(np.float64)[cols] if db is not None else None
-
+def _check_columns(wl, policy, y_bits, dx_bits, cols, label):
+    """Oracle and per-element rules on columns `cols`: y and dx under the
+    one-ulp rule (asserted here), and the pieces of the gradient checks
+    (the oracle's dw / db on these columns and, under "bf16", the flip
+    bounds).  y_bits / dx_bits hold the GPU results of exactly `cols`."""
+    y_h = oracle.decode_bf16(y_bits)
+    dx_h = oracle.decode_bf16(dx_bits)
     x64 = oracle.decode_bf16(wl.x[:, cols])
     dy64 = oracle.decode_bf16(wl.dy[:, cols])
     w64 = oracle.decode_param(wl.w, wl.w_dtype)[cols]
     b64 = oracle.decode_param(wl.b, wl.b_dtype)[cols] if wl.b is not None else None
     f = oracle.forward(x64, w64, b64, wl.cu)
     g = oracle.backward(x64, w64, b64, wl.cu, dy64, policy)
-
-    rep = {"label": label, "policy": policy}
+    rep = {}
     rep["y"] = tol.check_ulp(label + " y", y_h, f["y"], tol.allowance_y(f["p"], f["pabs"], f["y"]))
     a_dpre = tol.allowance_dpre(f["p"], f["pabs"], dy64, g["dpre"], policy)
     rep["dx"] = tol.check_ulp(label + " dx (%s)" % policy, dx_h, g["dx"],
                               tol.allowance_dx(w64, wl.cu, a_dpre, g["dpre"]))
-    bound = tol.BOUND[policy]
     if policy == "bf16":
         flip = tol.bf16_flip(f["p"], f["pabs"], dy64)
         fw, fb = tol.flip_bound_grads(flip, x64, wl.cu)
         rep["flip_elems"] = int(np.count_nonzero(flip))
     else:
         fw, fb = np.zeros_like(g["dw"]), np.zeros_like(g["db"])
-    rep["dw_rel_l2"] = tol.rel_l2(dw_h, g["dw"])
-    lim = bound + np.linalg.norm(fw) / max(np.linalg.norm(g["dw"]), 1e-300)
+    return rep, g["dw"], g["db"], fw, fb
+
+
+def _check_gradients(label, policy, dw_h, db_h, dw64, db64, fw, fb, rep):
+    bound = tol.BOUND[policy]
+    rep["dw_rel_l2"] = tol.rel_l2(dw_h, dw64)
+    lim = bound + np.linalg.norm(fw) / max(np.linalg.norm(dw64), 1e-300)
     assert rep["dw_rel_l2"] <= lim, "%s dweight rel-L2 %.3e > %.3e" % (label, rep["dw_rel_l2"], lim)
     if db_h is not None:
-        rep["db_rel_l2"] = tol.rel_l2(db_h, g["db"])
-        lim = bound + np.linalg.norm(fb) / max(np.linalg.norm(g["db"]), 1e-300)
+        rep["db_rel_l2"] = tol.rel_l2(db_h, db64)
+        lim = bound + np.linalg.norm(fb) / max(np.linalg.norm(db64), 1e-300)
         assert rep["db_rel_l2"] <= lim, "%s dbias rel-L2 %.3e > %.3e" % (label, rep["db_rel_l2"], lim)
+
+
+def compare(wl, policy, y, dx, dw, db, cols=None, *, label=""):
+    """Check GPU outputs (device tensors) on columns `cols` (all if None) against the oracle."""
+    torch = torch_mod()
+    if cols is None:
+        cols = np.arange(wl.C)
+    cols_t = torch.from_numpy(cols.astype(np.int64)).to(y.device)
+    y_bits = bf16_bits(y.index_select(1, cols_t))
+    dx_bits = bf16_bits(dx.index_select(1, cols_t))
+    dw_h = dw.float().cpu().numpy().astype(np.float64)[cols]
+    db_h = db.float().cpu().numpy().astype(np.float64)[cols] if db is not None else None
+    rep, dw64, db64, fw, fb = _check_columns(wl, policy, y_bits, dx_bits, cols, label)
+    rep = {"label": label, "policy": policy, **rep}
+    _check_gradients(label, policy, dw_h, db_h, dw64, db64, fw, fb, rep)
+    say("PARITY", rep)
+    return rep
+
+
+def compare_all(wl, policy, y, dx, dw, db, *, label="", block=256, workers=16):
+    """Every element of every column, as compare() does, for full-size
+    workloads: the columns are checked in blocks of `block` (channels are
+    independent, so the oracle on a block is the oracle on those columns),
+    `workers` blocks at a time on host threads (the oracle's C code and
+    numpy's array operations release the interpreter lock).  The gradients'
+    rel-L2 and flip bounds are assembled over all columns."""
+    from concurrent.futures import ThreadPoolExecutor
+    y_bits, dx_bits = bf16_bits(y), bf16_bits(dx)
+    dw_h = dw.float().cpu().numpy().astype(np.float64)
+    db_h = db.float().cpu().numpy().astype(np.float64) if db is not None else None
+    blocks = [np.arange(c0, min(c0 + block, wl.C)) for c0 in range(0, wl.C, block)]
+    done = [0]
+
+    def one(cols):
+        r = _check_columns(wl, policy, np.ascontiguousarray(y_bits[:, cols]),
+                           np.ascontiguousarray(dx_bits[:, cols]), cols,
+                           "%s cols %d..%d" % (label, cols[0], cols[-1]))
+        done[0] += 1
+        say("  block %d/%d (cols %d..%d): y %d beyond 1 ulp, dx %d beyond 1 ulp"
+            % (done[0], len(blocks), cols[0], cols[-1], r[0]["y"]["beyond_1ulp"],
+               r[0]["dx"]["beyond_1ulp"]))
+        return r
+
+    with ThreadPoolExecutor(min(workers, len(blocks))) as pool:
+        parts = list(pool.map(one, blocks))
+    rep = {"label": label, "policy": policy}
+    for key in ("y", "dx"):
+        rs = [p[0][key] for p in parts]
+        rep[key] = {"n": sum(r["n"] for r in rs), "violations": sum(r["violations"] for r in rs),
+                    "beyond_1ulp": sum(r["beyond_1ulp"] for r in rs),
+                    "max_ulps": max(r["max_ulps"] for r in rs)}
+    if policy == "bf16":
+        rep["flip_elems"] = sum(p[0]["flip_elems"] for p in parts)
+    dw64 = np.concatenate([p[1] for p in parts])
+    db64 = np.concatenate([p[2] for p in parts])
+    fw = np.concatenate([p[3] for p in parts])
+    fb = np.concatenate([p[4] for p in parts])
+    _check_gradients(label, policy, dw_h, db_h, dw64, db64, fw, fb, rep)
     say("PARITY", rep)
     return rep

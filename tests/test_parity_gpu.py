@@ -168,6 +168,27 @@ def test_full_size_sampled(torch_cuda, name, policy):
     torch.cuda.empty_cache()
 
 
+# Every element of generic (seeded random) full-size inputs, in the launch
+# configuration the benchmark times: (workload, policy, column block).
+FULL_ALL = [("headline", "bf16", 256), ("headline", "fp32", 256),
+            ("stress", "bf16", 32), ("stress", "fp32", 32)]
+
+
+@pytest.mark.parametrize("name,policy,block", FULL_ALL, ids=["%s-%s" % f[:2] for f in FULL_ALL])
+def test_full_size_all_elements(torch_cuda, name, policy, block):
+    """All S x C elements of y and dx, and all of dweight / dbias, against
+    the oracle under the same rules as the small cases (the oracle runs on
+    blocks of columns on host threads)."""
+    torch = torch_cuda
+    G.say("CASE full, every element", name, policy)
+    wl = G.named(name)
+    dev = G.to_device(wl)
+    y, dx, dw, db = G.run_gpu(dev, policy)
+    G.compare_all(wl, policy, y, dx, dw, db, label=name + " all", block=block, workers=16)
+    del dev, y, dx, dw, db
+    torch.cuda.empty_cache()
+
+
 def test_zero_tokens_launch_nothing(torch_cuda):
     torch = torch_cuda
     import varlen_depthwise_causal_amd as vdc

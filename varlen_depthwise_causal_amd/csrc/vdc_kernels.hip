@@ -368,17 +368,6 @@ __device__ __forceinline__ float sigmoid_scaled64(float z) {
                                __builtin_amdgcn_exp2f(__builtin_fmaf(z, -kLog2e, -64.0f)));
 }
 
-// SiLU'(z) = s * (1 + z * (1 - s)) with s = 1 / (1 + e), e = exp(-z).
-// 1 - s is formed as e * s, which keeps its relative accuracy where s is
-// close to 1; forming it as 1 - s (or z - z*s) would leave an absolute
-// error of about z * 2^-24 in SiLU' for large positive z.
-__device__ __forceinline__ float silu_grad_fast(float z) {
-  const float e = __builtin_amdgcn_exp2f(-z * kLog2e);
-  const float s = __builtin_amdgcn_rcpf(1.0f + e);
-  const float t = z * (e * s);
-  return __builtin_fmaf(t, s, s);
-}
-
 // SiLU'(z) for z < kDeep: there 1 - s == 1 in binary32, so s * (1 + z).
 __device__ __forceinline__ float silu_grad_deep(float z) {
   return (sigmoid_scaled64(z) * (1.0f + z)) * 0x1p-64f;
@@ -431,6 +420,54 @@ constexpr float cx_silu_grad(double z) {
   double s = 1.0 / (1.0 + e);
   double one_minus_s = e / (1.0 + e);
   return float(s * (1.0 + z * one_minus_s));
+}
+
+// SiLU' near its zero.  SiLU'(z) = s (1 + z (1 - s)) vanishes at z0 ~ -1.2785,
+// where any binary32 evaluation of the bracket cancels: its absolute error
+// stays near 2^-24 while its value goes to zero.  There the "fp32" policy
+// takes the Taylor series of SiLU' about z0 instead, in d = z - z0 formed
+// from a two-float split of z0 (z - z0_hi is exact near z0).
+struct NearZero {
+  float z0_hi, z0_lo;
+  float c1, c2, c3;  // second, third / 2 and fourth / 6 derivative of SiLU at z0
+};
+
+constexpr NearZero make_near_zero() {
+  // z0 solves 1 + z / (1 + e^z) = 0 (the bracket of SiLU'), by Newton's method.
+  double z = -1.28;
+  for (int it = 0; it < 40; ++it) {
+    const double ez = cx_exp(z);
+    const double g = 1.0 + z / (1.0 + ez);
+    const double dg = 1.0 / (1.0 + ez) - z * ez / ((1.0 + ez) * (1.0 + ez));
+    z -= g / dg;
+  }
+  const double s = 1.0 / (1.0 + cx_exp(-z));
+  const double s1 = s * (1.0 - s);                         // sigmoid, first derivative
+  const double s2 = s1 * (1.0 - 2.0 * s);                  // second
+  const double s3 = s2 * (1.0 - 2.0 * s) - 2.0 * s1 * s1;  // third
+  const double s4 = s3 * (1.0 - 2.0 * s) - 6.0 * s1 * s2;  // fourth
+  NearZero n{};
+  n.z0_hi = float(z);
+  n.z0_lo = float(z - double(n.z0_hi));
+  // Derivatives of SiLU(z) = z s: the (k+1)-th is (k+1) s^(k) + z s^(k+1).
+  n.c1 = float(2.0 * s1 + z * s2);
+  n.c2 = float((3.0 * s2 + z * s3) / 2.0);
+  n.c3 = float((4.0 * s3 + z * s4) / 6.0);
+  return n;
+}
+
+constexpr NearZero kNearZero = make_near_zero();
+// |1 + z (1 - s)| below this selects the series: the bracket's derivative
+// at z0 is 1, so this is |z - z0| < ~2^-10, where the series' first
+// omitted term is below 2^-40 |SiLU'|, and outside it the binary32
+// bracket keeps a relative error below 2^-12.
+constexpr float kNearZeroU = 0x1p-10f;
+
+__device__ __forceinline__ float silu_grad_series(float z) {
+  const float d = (z - kNearZero.z0_hi) - kNearZero.z0_lo;
+  float t = __builtin_fmaf(d, kNearZero.c3, kNearZero.c2);
+  t = __builtin_fmaf(d, t, kNearZero.c1);
+  return d * t;
 }
 
 struct alignas(16) SiluGradTable {
@@ -765,17 +802,36 @@ __device__ __forceinline__ void dpre_row(const float (&p)[V], const float (&dyv)
       dp[2 * d + 1] = dyv[2 * d + 1] * *reinterpret_cast<const float*>(base + o1);
     }
   } else {
-    float zmin = 0.0f;
+    // SiLU'(z) = s u, s = 1 / (1 + e), e = exp(-z), u = 1 + z (1 - s) as
+    // one fused multiply-add.  1 - s is formed as e s, which keeps its
+    // relative accuracy where s is close to 1 (1 - s itself would leave an
+    // absolute error of about z 2^-24 in SiLU' for large positive z).  Two
+    // rare cases take a wave-uniform branch: z below kDeep (s leaves the
+    // binary32 normal range) and |u| below kNearZeroU (the bracket cancels
+    // near SiLU's zero; the series about the zero is exact there).
+    float zmin = 0.0f, umin = 1.0f, r[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
-      zmin = __builtin_fminf(zmin, p[i]);
-      dp[i] = dyv[i] * silu_grad_fast(p[i]);
+      const float z = p[i];
+      const float e = __builtin_amdgcn_exp2f(-z * kLog2e);
+      const float sg = __builtin_amdgcn_rcpf(1.0f + e);
+      const float u = __builtin_fmaf(z, e * sg, 1.0f);
+      zmin = __builtin_fminf(zmin, z);
+      umin = __builtin_fminf(umin, __builtin_fabsf(u));
+      r[i] = sg * u;
     }
-    if (zmin < kDeep) {
+    if (!wave_none(zmin < kDeep || umin < kNearZeroU)) {
 #pragma unroll
-      for (int i = 0; i < V; ++i)
-        if (p[i] < kDeep) dp[i] = dyv[i] * silu_grad_deep(p[i]);
+      for (int i = 0; i < V; ++i) {
+        const float z = p[i];
+        const float e = __builtin_amdgcn_exp2f(-z * kLog2e);
+        const float u = __builtin_fmaf(z, e * __builtin_amdgcn_rcpf(1.0f + e), 1.0f);
+        if (__builtin_fabsf(u) < kNearZeroU) r[i] = silu_grad_series(z);
+        if (z < kDeep) r[i] = silu_grad_deep(z);
+      }
     }
+#pragma unroll
+    for (int i = 0; i < V; ++i) dp[i] = dyv[i] * r[i];
   }
 }
 
