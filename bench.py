@@ -483,7 +483,7 @@ def main():
                 "GB_s": round(bwd_gbs, 2), "frac_of_peak": round(bwd_gbs / HBM_PEAK_GBS, 4),
                 "mtokens_per_s": round(wl.S / (bwd_ms * 1e-3) / 1e6, 3),
                 "algorithmic_bytes": bb, "plan": g["plan_bwd"],
-                "partial_bytes": 2 * g["plan_bwd"]["bands"] * 5 * wl.C * g["plan_bwd"]["acc_bytes"]},
+                "partial_bytes": 2 * g["plan_bwd"]["prows"] * 5 * wl.C * g["plan_bwd"]["acc_bytes"]},
         "roofline": roofline("conv1d_bwd (bwd_main_kernel then bwd_reduce_kernel, one call)",
                              bb, bwd_ms, traffic, ("bwd_main_kernel", "bwd_reduce_kernel")),
         "roofline_fwd": roofline("fwd_kernel", fb, fwd_ms, traffic, ("fwd_kernel",)),

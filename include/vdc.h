@@ -101,8 +101,9 @@ enum vdc_status {
  * [F] Parameters workspace and [B] Parameters workspace: one size that
  * serves every route of the direction.  VDC_FWD: the forward keeps no
  * counters and needs no workspace, so the answer is 0 (conv1d_fwd accepts
- * workspace = NULL).  VDC_BWD: room for the per-band FP32 / FP64 partial
- * rows of dweight and dbias for every policy, at this (S, C), plus the
+ * workspace = NULL).  VDC_BWD: room for the FP32 / FP64 partial rows of
+ * dweight and dbias (one per band of tokens, or per workgroup of the main
+ * kernel when 256 <= C < 1024) for every policy, at this (S, C), plus the
  * FP64 sums of the reduce's first stage when there are more than 2048
  * partial rows; the backward writes every byte it later reads, so the
  * buffer needs no zeroing ([B] Parameters workspace).
@@ -219,14 +220,15 @@ const char *conv1d_status_string(int status);
 /*
  * conv1d_plan - the launch plan a call with these sizes would use
  * (introspection for tests and benchmarks; enqueues nothing).
- * Fills out[0..9] = { rows per band, bands (= partial rows of the
- * backward), lanes (bands * C / channels per lane), main-kernel workgroups,
- * threads per workgroup, partial element bytes (0 forward, 4 or 8
- * backward), reduce-kernel workgroups, reduce chunks, channels per lane,
- * first-stage reduce row ranges (0 when the reduce is one launch) }.
+ * Fills out[0..10] = { rows per band, bands, lanes (bands * C / channels
+ * per lane), main-kernel workgroups, threads per workgroup, partial
+ * element bytes (0 forward, 4 or 8 backward), reduce-kernel workgroups,
+ * reduce chunks, channels per lane, first-stage reduce row ranges (0 when
+ * the reduce is one launch), partial rows of the backward (0 forward:
+ * one per band, or one per workgroup when 256 <= C < 1024) }.
  * Returns a vdc_status.
  */
-int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int64_t out[10]);
+int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int64_t out[11]);
 
 /* conv1d_launch_count - kernels this process has launched through the
  * library so far (a diagnostic counter, e.g. to check that S == 0

@@ -138,20 +138,22 @@ def test_workspace_bytes(lib):
     assert lib.workspace_bytes(7, 100, 64) == 0
     for S, C in ((1000, 64), (65536, 4096), (262144, 520), (131072, 8192), (1, 8)):
         n = lib.workspace_bytes(BWD, S, C)
-        out = (ctypes.c_int64 * 10)()
+        out = (ctypes.c_int64 * 11)()
         assert lib.conv1d_plan(BWD, S, C, 1, out) == OK
-        rows, bands = out[0], out[1]
+        rows, bands, prows = out[0], out[1], out[10]
         assert bands == -(-S // rows)
-        assert n == bands * 5 * C * 8                        # FP64 partials of every band
+        # FP64 partials: one row per band, or per workgroup when 256 <= C < 1024
+        assert prows == (out[3] if 256 <= C < 1024 else bands)
+        assert n == prows * 5 * C * 8
         assert lib.conv1d_plan(BWD, S, C, 0, out) == OK
-        assert out[5] == 4 and n >= out[1] * 5 * C * 4
+        assert out[5] == 4 and n >= out[10] * 5 * C * 4
 
 
 def test_plans_depend_on_shape_only(lib):
     for d in (FWD, BWD):
         for S, C in ((65536, 4096), (262144, 520), (1000, 64), (2 ** 31 - 1, 8),
                      (2 ** 27, 8), (2 ** 24, 24), (2 ** 20, 2 ** 20), (5, 8)):
-            a, b = (ctypes.c_int64 * 10)(), (ctypes.c_int64 * 10)()
+            a, b = (ctypes.c_int64 * 11)(), (ctypes.c_int64 * 11)()
             assert lib.conv1d_plan(d, S, C, 0, a) == OK
             assert lib.conv1d_plan(d, S, C, 0, b) == OK
             assert list(a) == list(b)
@@ -167,12 +169,13 @@ def test_plans_depend_on_shape_only(lib):
             block_rows = (-(-threads // (C // vec)) + 1) * rows + 6
             assert block_rows < 32 * 1023
             assert bands * rows >= S and (bands - 1) * rows < max(S, 1)
-            stage1 = a[9]
+            stage1, prows = a[9], a[10]
             if d == BWD:
-                assert stage1 == (0 if bands <= 2048 else -(-bands // 2048))
-                assert lib.workspace_bytes(BWD, S, C) == (bands + stage1) * 5 * C * 8
+                assert prows == (blocks if 64 <= C // vec < threads else bands)
+                assert stage1 == (0 if prows <= 2048 else -(-prows // 2048))
+                assert lib.workspace_bytes(BWD, S, C) == (prows + stage1) * 5 * C * 8
             else:
-                assert stage1 == 0
+                assert stage1 == 0 and prows == 0
 
 
 def test_plan_invariants_over_random_shapes(lib):
@@ -189,7 +192,7 @@ def test_plan_invariants_over_random_shapes(lib):
         S = int(np.exp(rng.uniform(0.0, np.log(2.0 ** 31 - 1))))
         C = 8 * int(np.exp(rng.uniform(0.0, np.log(2.0 ** 17))))
         for d, group in ((FWD, 16), (BWD, 8)):
-            out = (ctypes.c_int64 * 10)()
+            out = (ctypes.c_int64 * 11)()
             rc = lib.conv1d_plan(d, S, C, 0, out)
             if rc != OK:
                 assert rc == EINVAL
@@ -244,8 +247,8 @@ def test_noalloc_scratch_covers_the_workloads(lib):
     fits = 0
     for C in (8, 64, 128, 136, 520, 1000, 4096, 8192, 65536):
         for S in (1, 1000, 65536, 1 << 20, 1 << 24, 2 ** 31 - 1):
-            out = (ctypes.c_int64 * 10)()
-            if lib.conv1d_plan(BWD, S, C, 1, out) == OK and out[1] * C <= 1 << 18:
+            out = (ctypes.c_int64 * 11)()
+            if lib.conv1d_plan(BWD, S, C, 1, out) == OK and out[10] * C <= 1 << 18:
                 assert lib.workspace_bytes(BWD, S, C) <= scratch, (S, C)
                 fits += 1
     assert fits > 30

@@ -107,12 +107,12 @@ def workspace_bytes(direction: str, S: int, C: int) -> int:
 def conv1d_plan(direction: str, S: int, C: int, policy: str = "bf16") -> dict:
     """The launch plan the library picks for these sizes (introspection)."""
     d = {"fwd": VDC_FWD, "bwd": VDC_BWD}[direction]
-    out = (ctypes.c_int64 * 10)()
+    out = (ctypes.c_int64 * 11)()
     rc = load().conv1d_plan(d, int(S), int(C), _POLICIES[policy], out)
     if rc:
         raise VdcError(rc, "conv1d_plan")
     keys = ("rows", "bands", "lanes", "blocks", "threads", "acc_bytes", "red_blocks", "red_chunks",
-            "vec", "red_stage1")
+            "vec", "red_stage1", "prows")
     return dict(zip(keys, (int(v) for v in out)))
 
 

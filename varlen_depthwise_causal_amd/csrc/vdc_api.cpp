@@ -89,9 +89,16 @@ Plan make_plan(int dir, int64_t S, int64_t C, int policy) {
   p.blocks = (int32_t)ceil_div(p.lanes, kBlock);
   p.acc_bytes = dir == VDC_FWD ? 0 : (policy == VDC_SILU_GRAD_FP32 ? 8 : 4);
   p.red_blocks = dir == VDC_FWD ? 0 : (int32_t)ceil_div(5 * C, kRedOut);
-  p.red_stage1 = (dir == VDC_FWD || p.bands <= kRedBlockRows)
+  // Backward partial rows.  With 64 <= C/V < kBlock, a workgroup's lanes
+  // cover every channel (one or two bands' worth, some channels twice), so
+  // the workgroup sums its lanes' band totals in a fixed order and writes
+  // one row: fewer rows than bands where bands are short.
+  const int64_t nvec = C / p.vec;
+  p.wg_rows = (dir == VDC_BWD && nvec >= 64 && nvec < kBlock) ? 1 : 0;
+  p.prows = dir == VDC_FWD ? 0 : (p.wg_rows ? p.blocks : p.bands);
+  p.red_stage1 = (dir == VDC_FWD || p.prows <= kRedBlockRows)
                      ? 0
-                     : (int32_t)ceil_div(p.bands, kRedBlockRows);
+                     : (int32_t)ceil_div(p.prows, kRedBlockRows);
   return p;
 }
 
@@ -125,10 +132,10 @@ extern "C" size_t workspace_bytes(int direction, int64_t S, int64_t C) {
   // then the binary64 sums of the reduce's first stage when it has one.
   const Plan p = make_plan(VDC_BWD, S, C, VDC_SILU_GRAD_FP32);
   if (!plan_fits(p)) return 0;
-  return ((size_t)p.bands + (size_t)p.red_stage1) * 5 * (size_t)C * 8;
+  return ((size_t)p.prows + (size_t)p.red_stage1) * 5 * (size_t)C * 8;
 }
 
-extern "C" int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int64_t out[10]) {
+extern "C" int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int64_t out[11]) {
   if (!out) return VDC_EINVAL;
   if (direction != VDC_FWD && direction != VDC_BWD) return VDC_EINVAL;
   if (direction == VDC_BWD && policy != VDC_SILU_GRAD_BF16 && policy != VDC_SILU_GRAD_FP32)
@@ -147,6 +154,7 @@ extern "C" int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int6
   out[7] = kRedChunks;
   out[8] = p.vec;
   out[9] = p.red_stage1;
+  out[10] = p.prows;
   return VDC_OK;
 }
 
@@ -316,6 +324,7 @@ int bwd_enqueue(const BwdCall& c, void* workspace, hipStream_t stream) {
   a.rows = plan.rows;
   a.bands = plan.bands;
   a.blocks = plan.blocks;
+  a.wg_rows = plan.wg_rows;
   g_launches.fetch_add(1, std::memory_order_relaxed);
   if (launch_bwd_main(plan, a, c.bias != nullptr, fp32_policy, stream) != hipSuccess)
     return VDC_EHIP;
@@ -324,7 +333,7 @@ int bwd_enqueue(const BwdCall& c, void* workspace, hipStream_t stream) {
   r.part = workspace;
   r.dw = c.dweight;
   r.db = c.dbias;
-  r.P = plan.bands;
+  r.P = plan.prows;
   r.C = (int32_t)c.C;
   r.dw_bf16 = c.dw_dtype == VDC_BF16;
   r.db_bf16 = c.db_dtype == VDC_BF16;
@@ -332,7 +341,7 @@ int bwd_enqueue(const BwdCall& c, void* workspace, hipStream_t stream) {
   if (plan.red_stage1 > 0) {
     // Many partial rows: sums of kRedBlockRows-row ranges first, into the
     // workspace after the largest partial-row area, then one pass over them.
-    r.inter = static_cast<char*>(workspace) + (size_t)plan.bands * 5 * (size_t)c.C * 8;
+    r.inter = static_cast<char*>(workspace) + (size_t)plan.prows * 5 * (size_t)c.C * 8;
     g_launches.fetch_add(1, std::memory_order_relaxed);
     if (launch_bwd_reduce_rows(plan, r, part_f64, stream) != hipSuccess) return VDC_EHIP;
     r.part = r.inter;

@@ -68,6 +68,8 @@ struct Plan {
   int32_t acc_bytes;   // backward partial element: 4 (FP32) or 8 (FP64)
   int32_t red_blocks;  // reduce workgroups per row range (kRedOut outputs each)
   int32_t red_stage1;  // first-stage row ranges (0: the reduce is one pass)
+  int32_t wg_rows;     // backward: 1 = one partial row per workgroup, 0 = per band
+  int32_t prows;       // backward partial rows: blocks (wg_rows) or bands
 };
 
 struct FwdArgs {
@@ -104,6 +106,7 @@ struct BwdArgs {
   int32_t rows;
   int32_t bands;
   int32_t blocks;      // workgroups with lanes (the grid may be padded)
+  int32_t wg_rows;     // 1: one partial row per workgroup (see Plan)
 };
 
 struct ReduceArgs {

@@ -896,8 +896,11 @@ void bwd_main_kernel(BwdArgs a) {
   typedef typename VT::raw Raw;
   __shared__ __attribute__((aligned(16))) float lut_lds[kBf16Policy ? 2 * kLutN : 4];
   __shared__ DocMask dmask;
-  // Rows of a masked group, [row][thread]: x in words 0-1, dy in 2-3.
-  __shared__ u32x4 stage[kBwdGroup * kBlock];
+  // Rows of a masked group, [row][thread]: x in words 0-1, dy in 2-3; at
+  // the end, each thread's band totals, [total][thread].
+  constexpr int kStageRows = kBwdGroup > 5 * (int)sizeof(Acc) / 4 ? kBwdGroup
+                                                                   : 5 * (int)sizeof(Acc) / 4;
+  __shared__ u32x4 stage[kStageRows * kBlock];
   Lane L;
   const uint32_t place = block_place();
   if (place >= (uint32_t)a.blocks) return;  // padding workgroup: no lane
@@ -947,7 +950,17 @@ void bwd_main_kernel(BwdArgs a) {
   // barriers make it visible).
   if (kBf16Policy) lut_stage_store(lut_stage, lut_lds);
   build_doc_mask(dmask, place, cu_pre, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
-  if (!active) return;
+  // Lanes past the last band have nothing to compute; with one partial row
+  // per workgroup they still join its final sum (one barrier).
+  if (!active && !a.wg_rows) return;
+  // Band total j of lane l in LDS: in the lane's own 16-byte column of
+  // `stage` (the masked path uses only the thread's own column too, so a
+  // thread writing its totals disturbs no thread still in its loop).
+  constexpr int kPerSlot = 16 / (int)sizeof(Acc);
+  auto slot = [&](int j, uint32_t l) -> Acc* {
+    return reinterpret_cast<Acc*>(stage + (j / kPerSlot) * kBlock + l) + j % kPerSlot;
+  };
+  if (active) {
   float w[4][V], bv[V];
   unpack_params<V>(praw, a.w_bf16, a.b_bf16, w, bv);
 
@@ -1076,13 +1089,47 @@ void bwd_main_kernel(BwdArgs a) {
   }
   run(xa, da, a.rows, 3, false);
 
-  // One partial row per band: part[band][k][c].
-  Acc* part = reinterpret_cast<Acc*>(a.part) + (int64_t)L.band * 5 * a.C + L.vec * V;
+  if (!a.wg_rows) {
+    // One partial row per band: part[band][k][c].
+    Acc* part = reinterpret_cast<Acc*>(a.part) + (int64_t)L.band * 5 * a.C + L.vec * V;
 #pragma unroll
-  for (int k = 0; k < 5; ++k) {
-    Acc* dst = part + (int64_t)k * a.C;
+    for (int k = 0; k < 5; ++k) {
+      Acc* dst = part + (int64_t)k * a.C;
 #pragma unroll
-    for (int i = 0; i < V; ++i) dst[i] = acc.total(k, i);
+      for (int i = 0; i < V; ++i) dst[i] = acc.total(k, i);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+#pragma unroll
+      for (int i = 0; i < V; ++i) *slot(k * V + i, threadIdx.x) = acc.total(k, i);
+  }
+  }  // active
+  else {
+#pragma unroll
+    for (int j = 0; j < 5 * V; ++j) *slot(j, threadIdx.x) = (Acc)0;
+  }
+  if (!a.wg_rows) return;
+
+  // One partial row per workgroup: part[place][k][c].  The workgroup's lanes
+  // cover every vector of channels (C/V < kBlock), some twice; thread t sums
+  // vector t's lanes in increasing lane order, that is in increasing band
+  // order, in binary64, and rounds once to the partial element type.
+  __syncthreads();
+  if ((int32_t)threadIdx.x < a.nvec) {
+    const uint32_t nvec = (uint32_t)a.nvec;
+    const uint32_t first = (threadIdx.x + nvec - (place * (uint32_t)kBlock) % nvec) % nvec;
+    double s[5 * V];
+#pragma unroll
+    for (int j = 0; j < 5 * V; ++j) s[j] = 0.0;
+    for (uint32_t l = first; l < (uint32_t)kBlock; l += nvec)
+#pragma unroll
+      for (int j = 0; j < 5 * V; ++j) s[j] += (double)*slot(j, l);
+    Acc* part = reinterpret_cast<Acc*>(a.part) + (int64_t)place * 5 * a.C + threadIdx.x * V;
+#pragma unroll
+    for (int k = 0; k < 5; ++k)
+#pragma unroll
+      for (int i = 0; i < V; ++i) part[(int64_t)k * a.C + i] = (Acc)s[k * V + i];
   }
 }
 
