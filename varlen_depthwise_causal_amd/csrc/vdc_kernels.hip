@@ -458,10 +458,11 @@ constexpr NearZero make_near_zero() {
 
 constexpr NearZero kNearZero = make_near_zero();
 // |1 + z (1 - s)| below this selects the series: the bracket's derivative
-// at z0 is 1, so this is |z - z0| < ~2^-10, where the series' first
-// omitted term is below 2^-40 |SiLU'|, and outside it the binary32
-// bracket keeps a relative error below 2^-12.
-constexpr float kNearZeroU = 0x1p-10f;
+// at z0 is 1, so this is |z - z0| < ~2^-12.  The bracket's absolute error
+// is a few 2^-24 (from exp, the reciprocal and the products), so outside
+// the window its relative error stays near 2^-10, a quarter of a BF16 ulp;
+// inside, the series' first omitted term is below 2^-40 |SiLU'|.
+constexpr float kNearZeroU = 0x1p-12f;
 
 __device__ __forceinline__ float silu_grad_series(float z) {
   const float d = (z - kNearZero.z0_hi) - kNearZero.z0_lo;
