@@ -185,8 +185,9 @@ int conv1d_bwd(const void *x, const void *weight, int w_dtype,
  * device array inside the library of conv1d_noalloc_scratch_bytes() bytes
  * (16 MiB), one copy per GPU, held until the process ends.  The first call
  * on a device looks up that device's copy (with hipGetSymbolAddress; the
- * device of `stream` is made current for the lookup and restored after);
- * no call allocates or frees anything.
+ * device of `stream` is made current for the lookup and restored after),
+ * so make that first call outside any stream capture; no call allocates or
+ * frees anything, and later calls may be captured into a HIP graph.
  *
  * A problem whose workspace_bytes(VDC_BWD, S, C) exceeds the array returns
  * VDC_ESCRATCH before anything is enqueued.  Every launch plan whose bands

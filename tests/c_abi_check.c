@@ -111,11 +111,12 @@ int main(void)
     /* Host inputs: BF16 x, dy; FP32 weight, bias; int32 cu_seqlens. */
     const int64_t n = (int64_t)S * C;
     uint16_t *x = malloc(n * 2), *dy = malloc(n * 2), *y = malloc(n * 2), *dx = malloc(n * 2);
-    float w[C * 4], b[C], dw[C * 4], db[C];
+    uint16_t *dx2 = malloc(n * 2);
+    float w[C * 4], b[C], dw[C * 4], db[C], dw2[C * 4], db2[C];
     int32_t cu[D + 1];
     double *x64 = malloc(n * 8), *dy64 = malloc(n * 8), *y64 = malloc(n * 8), *dx64 = malloc(n * 8);
     double w64[C * 4], b64[C], dw64[C * 4], db64[C];
-    if (!x || !dy || !y || !dx || !x64 || !dy64 || !y64 || !dx64) {
+    if (!x || !dy || !y || !dx || !dx2 || !x64 || !dy64 || !y64 || !dx64) {
         fprintf(stderr, "c_abi_check: out of host memory\n");
         return 1;
     }
@@ -143,7 +144,7 @@ int main(void)
     orc_decode_bf16(dy, dy64, n);
 
     /* Device buffers; the caller owns all of them, workspace included. */
-    void *d_x, *d_dy, *d_y, *d_dx, *d_w, *d_b, *d_cu, *d_dw, *d_db, *d_ws;
+    void *d_x, *d_dy, *d_y, *d_dx, *d_w, *d_b, *d_cu, *d_dw, *d_db, *d_ws, *d_dx2, *d_dw2, *d_db2;
     const size_t ws = workspace_bytes(VDC_BWD, S, C);
     expect(ws > 0 && workspace_bytes(VDC_FWD, S, C) == 0, "workspace_bytes");
     HIP_CHECK(hipMalloc(&d_x, n * 2));
@@ -156,6 +157,9 @@ int main(void)
     HIP_CHECK(hipMalloc(&d_dw, sizeof dw));
     HIP_CHECK(hipMalloc(&d_db, sizeof db));
     HIP_CHECK(hipMalloc(&d_ws, ws));
+    HIP_CHECK(hipMalloc(&d_dx2, n * 2));
+    HIP_CHECK(hipMalloc(&d_dw2, sizeof dw2));
+    HIP_CHECK(hipMalloc(&d_db2, sizeof db2));
     HIP_CHECK(hipMemcpy(d_x, x, n * 2, hipMemcpyHostToDevice));
     HIP_CHECK(hipMemcpy(d_dy, dy, n * 2, hipMemcpyHostToDevice));
     HIP_CHECK(hipMemcpy(d_w, w, sizeof w, hipMemcpyHostToDevice));
@@ -213,13 +217,29 @@ int main(void)
         snprintf(what, sizeof what, "dweight and dbias (%s) within the rel-L2 bound",
                  kPolicies[q].name);
         expect(rw <= kPolicies[q].bound && rb <= kPolicies[q].bound, what);
+
+        /* The no-allocation entry point: the library's own workspace, the
+         * same kernels and plan, so bitwise the same outputs. */
+        expect(ws <= conv1d_noalloc_scratch_bytes(), "workspace fits the no-allocation array");
+        rc = conv1d_bwd_noalloc(d_x, d_w, VDC_F32, d_b, VDC_F32, d_cu, D, d_dy, S, C,
+                                kPolicies[q].policy, d_dx2, d_dw2, VDC_F32, d_db2, VDC_F32, stream);
+        snprintf(what, sizeof what, "conv1d_bwd_noalloc (%s) returns VDC_OK", kPolicies[q].name);
+        expect(rc == VDC_OK, what);
+        HIP_CHECK(hipStreamSynchronize(stream));
+        HIP_CHECK(hipMemcpy(dx2, d_dx2, n * 2, hipMemcpyDeviceToHost));
+        HIP_CHECK(hipMemcpy(dw2, d_dw2, sizeof dw2, hipMemcpyDeviceToHost));
+        HIP_CHECK(hipMemcpy(db2, d_db2, sizeof db2, hipMemcpyDeviceToHost));
+        snprintf(what, sizeof what, "conv1d_bwd_noalloc (%s) bitwise equal to conv1d_bwd",
+                 kPolicies[q].name);
+        expect(memcmp(dx2, dx, n * 2) == 0 && memcmp(dw2, dw, sizeof dw) == 0 &&
+                   memcmp(db2, db, sizeof db) == 0, what);
     }
 
     HIP_CHECK(hipStreamDestroy(stream));
-    void *bufs[] = {d_x, d_dy, d_y, d_dx, d_w, d_b, d_cu, d_dw, d_db, d_ws};
+    void *bufs[] = {d_x, d_dy, d_y, d_dx, d_w, d_b, d_cu, d_dw, d_db, d_ws, d_dx2, d_dw2, d_db2};
     for (size_t i = 0; i < sizeof bufs / sizeof bufs[0]; i++)
         HIP_CHECK(hipFree(bufs[i]));
-    free(x); free(dy); free(y); free(dx);
+    free(x); free(dy); free(y); free(dx); free(dx2);
     free(x64); free(dy64); free(y64); free(dx64);
     printf("%s\n", failures ? "c_abi_check: FAILED" : "c_abi_check: all checks passed");
     return failures ? 1 : 0;

@@ -129,3 +129,56 @@ def test_noalloc_refuses_oversized_problem(torch_cuda):
     torch.cuda.synchronize()
     assert vdc.conv1d_launch_count() == n0
     assert bool((dw == 3.0).all()) and bool((dx == 3.0).all())
+
+
+@pytest.mark.parametrize("policy", ["bf16", "fp32"])
+def test_noalloc_graph_replays_match_eager(torch_cuda, policy):
+    """The callers it is for: conv1d_bwd_noalloc captured into a HIP graph
+    (torch.cuda.CUDAGraph; nothing allocated during capture), replayed on new
+    inputs copied into the captured buffers, with eager calls of both entry
+    points between replays: every replay gives conv1d_bwd's bits."""
+    torch = torch_cuda
+    import varlen_depthwise_causal_amd as vdc
+    G.say("CASE noalloc graph", policy)
+    sets = [G.to_device(G.small_case(s, 6001, 520, "randint", "f32", "f32", (0.01, 60.0)))
+            for s in (41, 42, 43)]
+    static = {k: v.clone() for k, v in sets[0].items()}
+    S, C = static["x"].shape
+    dx = torch.empty_like(static["x"])
+    dw = torch.empty((C, 4), device="cuda")
+    db = torch.empty((C,), device="cuda")
+
+    def step():
+        vdc.conv1d_bwd_noalloc(static["x"], static["w"], static["cu"], static["dy"],
+                               bias=static["b"], silu_grad_preactivation=policy, dx=dx,
+                               dweight=dw, dbias=db)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # first call on the device outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep, inp in enumerate(sets + sets[:1]):
+        for k in static:
+            static[k].copy_(inp[k])
+        for t in (dx, dw, db):
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (dx, dw, db)]
+        ref = vdc.conv1d_bwd(inp["x"], inp["w"], inp["cu"], inp["dy"], bias=inp["b"],
+                             silu_grad_preactivation=policy,
+                             dweight=torch.empty((C, 4), device="cuda"),
+                             dbias=torch.empty((C,), device="cuda"))
+        # an eager no-allocation call between replays reuses the array
+        vdc.conv1d_bwd_noalloc(inp["x"], inp["w"], inp["cu"], inp["dy"], bias=inp["b"],
+                               silu_grad_preactivation=policy, dx=torch.empty_like(dx),
+                               dweight=torch.empty_like(dw), dbias=torch.empty_like(db))
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dx", "dw", "db"), got, ref):
+            assert torch.equal(a, b), "replay %d: %s differs from conv1d_bwd" % (rep, name)
