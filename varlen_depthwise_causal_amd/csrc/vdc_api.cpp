@@ -70,7 +70,7 @@ int32_t pick_vec(int dir) { return dir == VDC_FWD ? kFwdVec : kBwdVec; }
 
 int64_t pick_rows(int dir, int64_t S, int64_t C) {
   const int64_t nvec = C / pick_vec(dir);
-  const int64_t step = 2 * (dir == VDC_FWD ? kFwdGroup : kBwdGroup);
+  const int64_t step = 2 * (dir == VDC_FWD ? fwd_group(C) : kBwdGroup);
   const int64_t lanes_cap = kCUs * 4 * (dir == VDC_FWD ? kFwdWaves : kBwdWaves) * 64;
   const int64_t bands_cap = std::max<int64_t>(1, lanes_cap / nvec);
   int64_t rows = std::max<int64_t>(step, ceil_div(ceil_div(std::max<int64_t>(S, 1), bands_cap), step) * step);

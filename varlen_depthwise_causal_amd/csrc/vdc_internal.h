@@ -33,6 +33,13 @@ constexpr int kBlock = 256;
 #endif
 constexpr int kFwdGroup = VDC_FWD_GROUP;
 constexpr int kBwdGroup = VDC_BWD_GROUP;
+// The forward's row group for rows that are not a multiple of 128 bytes
+// with C < 1024 (Stress's C = 520): shorter groups there.
+#ifndef VDC_FWD_GROUP_SHORT
+#define VDC_FWD_GROUP_SHORT 8
+#endif
+constexpr int kFwdGroupShort = VDC_FWD_GROUP_SHORT;
+inline int fwd_group(int64_t C) { return ((C * 2) % 128 != 0 && C < 1024) ? kFwdGroupShort : kFwdGroup; }
 // Document-start bitmask of one workgroup, in 32-bit LDS words: the rows a
 // workgroup touches (its bands and three halo rows on each side) must span
 // fewer than 32 * (kDocMaskWords - 1) rows.

@@ -627,7 +627,7 @@ __device__ __forceinline__ typename Vec<V>::raw fwd_row(const float (&w)[4][V],
   return out;
 }
 
-template <bool kBias, bool kNt, int V>
+template <bool kBias, bool kNt, int V, int kFwdGroup>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kFwdWaves)))
 void fwd_kernel(FwdArgs a) {
   typedef Vec<V> VT;
@@ -1211,12 +1211,17 @@ template <int V>
 hipError_t launch_fwd_v(const Plan& plan, const FwdArgs& a, bool has_bias, hipStream_t s) {
   dim3 grid((uint32_t)padded_grid(plan.blocks)), block(kBlock);
   const bool nt = rows_line_aligned(a.C);
-  if (has_bias) {
-    if (nt) hipLaunchKernelGGL((fwd_kernel<true, true, V>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((fwd_kernel<true, false, V>), grid, block, 0, s, a);
+  const int group = fwd_group(a.C);
+  if (plan.rows % (2 * group)) return hipErrorInvalidValue;
+  if (group == kFwdGroupShort) {
+    if (has_bias) hipLaunchKernelGGL((fwd_kernel<true, false, V, kFwdGroupShort>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel<false, false, V, kFwdGroupShort>), grid, block, 0, s, a);
+  } else if (has_bias) {
+    if (nt) hipLaunchKernelGGL((fwd_kernel<true, true, V, kFwdGroup>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel<true, false, V, kFwdGroup>), grid, block, 0, s, a);
   } else {
-    if (nt) hipLaunchKernelGGL((fwd_kernel<false, true, V>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((fwd_kernel<false, false, V>), grid, block, 0, s, a);
+    if (nt) hipLaunchKernelGGL((fwd_kernel<false, true, V, kFwdGroup>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel<false, false, V, kFwdGroup>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
