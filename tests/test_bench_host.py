@@ -66,12 +66,14 @@ def test_counted_traffic_follows_digest_and_policy(tmp_path, monkeypatch):
 
 
 def test_committed_counters_parse():
-    """The committed summary holds one well-formed traffic record."""
+    """The committed summary holds one well-formed traffic record per
+    policy, all taken on the same kernel sources."""
     lines = [l for l in open(bench.COUNTERS_FILE).read().splitlines() if l.startswith("traffic-json: ")]
-    assert len(lines) == 1
-    rec = json.loads(lines[0][len("traffic-json: "):])
-    assert set(rec["bytes_per_launch"]) == {"fwd_kernel", "bwd_main_kernel", "bwd_reduce_kernel"}
-    assert rec["policy"] in ("bf16", "fp32")
+    recs = [json.loads(l[len("traffic-json: "):]) for l in lines]
+    assert sorted(r["policy"] for r in recs) == ["bf16", "fp32"]
+    assert len({r["sources"] for r in recs}) == 1
+    for rec in recs:
+        assert set(rec["bytes_per_launch"]) == {"fwd_kernel", "bwd_main_kernel", "bwd_reduce_kernel"}
 
 
 @pytest.mark.parametrize("argv, env", [(["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})])

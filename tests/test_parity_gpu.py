@@ -171,7 +171,8 @@ def test_full_size_sampled(torch_cuda, name, policy):
 # Every element of generic (seeded random) full-size inputs, in the launch
 # configuration the benchmark times: (workload, policy, column block).
 FULL_ALL = [("headline", "bf16", 256), ("headline", "fp32", 256),
-            ("stress", "bf16", 32), ("stress", "fp32", 32)]
+            ("stress", "bf16", 32), ("stress", "fp32", 32),
+            ("long", "fp32", 256), ("uniform", "bf16", 128)]
 
 
 @pytest.mark.parametrize("name,policy,block", FULL_ALL, ids=["%s-%s" % f[:2] for f in FULL_ALL])
