@@ -59,8 +59,9 @@ CPU_SAMPLE_CHANNELS = 4096
 # WRITE_SIZE, scaled by a plain copy's reading) for the kernels as built from
 # the sources whose digest the file records; ignored once the sources differ.
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "headline_counters.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "varlen_depthwise_causal_amd", "csrc", f)
-                  for f in ("vdc_kernels.hip", "vdc_internal.h", "vdc_api.cpp")]
+CSRC = os.path.join(ROOT, "varlen_depthwise_causal_amd", "csrc")
+KERNEL_SOURCES = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                        if f.endswith((".hip", ".h", ".cpp")))
 
 
 def algorithmic_bytes(wl, direction):

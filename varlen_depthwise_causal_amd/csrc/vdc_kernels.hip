@@ -39,6 +39,7 @@
 #include <stdint.h>
 
 #include "vdc_internal.h"
+#include "vdc_lines.h"
 #include "vdc_search.h"
 
 namespace vdc {
@@ -62,7 +63,9 @@ constexpr int kRsrcWord3 = 0x00020000;
 // 128-byte cache lines (rows a multiple of 128 bytes, C a multiple of 64)
 // they stream with "nt" (non-temporal).  Otherwise two neighbouring waves
 // share the lines at their boundary, and plain accesses, which let the
-// line stay in L2 for the second wave, move about 25% fewer bytes.
+// line stay in L2 for the second wave, move about 25% fewer bytes; the
+// forward's stores still stream the lines inside a wave's piece
+// (whole_line_bits).
 constexpr int kStream = 2;
 constexpr int kPlain = 0;
 
@@ -672,7 +675,19 @@ void fwd_kernel(FwdArgs a) {
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int g = 0; g < kFwdGroup; ++g) IO::store(ry, kNoRow + g * row_bytes, VT::zero());
+  for (int g = 0; g < kFwdGroup; ++g) {
+    IO::store(ry, kNoRow + g * row_bytes, VT::zero());
+    if (!kNt) IO::store(ry, kNoRow + g * row_bytes, VT::zero());
+  }
+  // Unaligned rows: the y stores of row g of every group stream where bit
+  // g & 7 is set, for the lines a wave writes alone (whole_line_bits); the
+  // lines at the ends of its piece, which another wave writes too, stay
+  // plain so that the two halves can meet in L2.
+  const uint32_t whole =
+      kNt ? 0u
+          : whole_line_bits((int64_t)(uintptr_t)(a.y + (int64_t)L.base_row * a.C) + L.off +
+                                3 * (int64_t)row_bytes,
+                            row_bytes, threadIdx.x & 63u, L.vec, a.nvec, V * 2);
 
   build_doc_mask(dmask, place, cu_pre, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
   if (!active) return;
@@ -734,9 +749,21 @@ void fwd_kernel(FwdArgs a) {
     }
     r += kFwdGroup;
   };
+  // On unaligned rows each row is two stores, one streaming and one plain,
+  // each lane's bytes in one of them (the other takes kNoRow): both are
+  // issued on every row, so every path keeps the same accesses in flight.
   auto store = [&](const Raw (&out)[kFwdGroup]) {
 #pragma unroll
-    for (int g = 0; g < kFwdGroup; ++g) IO::store(ry, off + g * row_bytes, out[g]);
+    for (int g = 0; g < kFwdGroup; ++g) {
+      const int32_t o = off + g * row_bytes;
+      if (kNt) {
+        IO::store(ry, o, out[g]);
+      } else {
+        const bool stream = (whole >> (g & 7)) & 1u;
+        Io<kStream>::store(ry, stream ? o : kNoRow, out[g]);
+        Io<kPlain>::store(ry, stream ? kNoRow : o, out[g]);
+      }
+    }
     off += kFwdGroup * row_bytes;
   };
   // T is a multiple of 2G (host rule).  The last pair's reload of A reads
