@@ -149,6 +149,31 @@ def test_workspace_bytes(lib):
         assert out[5] == 4 and n >= out[10] * 5 * C * 4
 
 
+def partials_share(lib, S, C, policy):
+    """Partial rows written by the main kernel and read by the reduce, as a
+    share of the backward's 6 S C activation bytes."""
+    out = (ctypes.c_int64 * 11)()
+    assert lib.conv1d_plan(BWD, S, C, policy, out) == OK
+    elem = 8 if policy == 1 else 4
+    return 2 * out[10] * 5 * C * elem / (6 * S * C)
+
+
+def test_partials_budget_of_the_workloads(lib):
+    """Partials stay within 2% of the backward's bytes where the bands are
+    long enough (tokens per partial row >= 333 under "bf16", 667 under
+    "fp32"): the headline, Long and Stress (per-workgroup rows at C = 520).
+    Uniform (S = 16384, C = 2048) has bands of 128 rows with the fixed grid
+    of 1024 waves and stays above, at the values stated here."""
+    from varlen_depthwise_causal_amd import workloads as W
+    for name in ("headline", "long", "stress"):
+        spec = W.SPECS[name]
+        for policy in (0, 1):
+            assert partials_share(lib, spec.S, spec.C, policy) <= 0.02, (name, policy)
+    spec = W.SPECS["uniform"]
+    assert partials_share(lib, spec.S, spec.C, 0) == pytest.approx(10 * 4 / (6 * 128))
+    assert partials_share(lib, spec.S, spec.C, 1) == pytest.approx(10 * 8 / (6 * 128))
+
+
 def test_plans_depend_on_shape_only(lib):
     for d in (FWD, BWD):
         for S, C in ((65536, 4096), (262144, 520), (1000, 64), (2 ** 31 - 1, 8),
