@@ -57,7 +57,7 @@ def _functions(mir):
 def test_every_kernel_is_scanned(final_mir):
     names = [n for n, _ in _functions(final_mir)]
     assert any("fwd_kernel" in n for n in names)
-    assert sum("bwd_main_kernel" in n for n in names) == 8
+    assert sum("bwd_main_kernel" in n for n in names) == 12
     assert sum("bwd_reduce_kernel" in n for n in names) == 2
 
 

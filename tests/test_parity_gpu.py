@@ -48,6 +48,10 @@ SMALL = [
     ("s1_c8", 15, 1, 8, [1], "f32", "f32", None),
     ("s2_c64", 16, 2, 64, [0, 1, 1], "bf16", "f32", None),
     ("s5_c136", 17, 5, 136, [2, 0, 3], "f32", None, None),
+    # backward lanes in column blocks (four bands per workgroup): 2048
+    # channels, bands of 48 rows, 105 bands (the last group of four holds
+    # one), a start every ~13 rows
+    ("c2048_groups", 18, 5000, 2048, "randint", "f32", "f32", None),
 ]
 
 

@@ -49,7 +49,8 @@ int64_t wave_span_rows(int64_t nvec, int64_t rows) {
 
 // Largest span, in rows, of one workgroup: the bands of its kBlock lanes
 // plus three halo rows on each side.  Its document starts must fit the
-// workgroup's LDS bitmask.
+// workgroup's LDS bitmask.  (Column-block workgroups span kCbBands bands of
+// fewer than kCbMaxRows rows, which always fit.)
 int64_t block_span_rows(int64_t nvec, int64_t rows) {
   return (ceil_div(kBlock, nvec) + 1) * rows + 6;
 }
@@ -92,10 +93,22 @@ Plan make_plan(int dir, int64_t S, int64_t C, int policy) {
   // Backward partial rows.  With 64 <= C/V < kBlock, a workgroup's lanes
   // cover every channel (one or two bands' worth, some channels twice), so
   // the workgroup sums its lanes' band totals in a fixed order and writes
-  // one row: fewer rows than bands where bands are short.
+  // one row: fewer rows than bands where bands are short.  With C/V a
+  // multiple of 64 and at least kBlock, and bands shorter than kCbMaxRows,
+  // lanes go in column blocks: a workgroup holds 64 vectors of kCbBands
+  // consecutive bands (one per wave) and sums their totals into one row
+  // segment, so a row stands for a group of kCbBands bands.  (With longer
+  // bands the partials are small anyway, and the linear map keeps a
+  // workgroup's waves on one band's rows, which measured faster where
+  // documents are dense.)
   const int64_t nvec = C / p.vec;
   p.wg_rows = (dir == VDC_BWD && nvec >= 64 && nvec < kBlock) ? 1 : 0;
-  p.prows = dir == VDC_FWD ? 0 : (p.wg_rows ? p.blocks : p.bands);
+  p.cb = (dir == VDC_BWD && bwd_column_blocks(nvec, p.rows)) ? 1 : 0;
+  if (p.cb) p.blocks = (int32_t)(ceil_div(p.bands, kCbBands) * (nvec / 64));
+  p.prows = dir == VDC_FWD ? 0
+            : p.wg_rows    ? p.blocks
+            : p.cb         ? (int32_t)ceil_div(p.bands, kCbBands)
+                           : p.bands;
   p.red_stage1 = (dir == VDC_FWD || p.prows <= kRedBlockRows)
                      ? 0
                      : (int32_t)ceil_div(p.prows, kRedBlockRows);
@@ -325,6 +338,7 @@ int bwd_enqueue(const BwdCall& c, void* workspace, hipStream_t stream) {
   a.bands = plan.bands;
   a.blocks = plan.blocks;
   a.wg_rows = plan.wg_rows;
+  a.cb = plan.cb;
   g_launches.fetch_add(1, std::memory_order_relaxed);
   if (launch_bwd_main(plan, a, c.bias != nullptr, fp32_policy, stream) != hipSuccess)
     return VDC_EHIP;

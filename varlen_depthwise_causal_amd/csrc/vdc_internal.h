@@ -63,6 +63,18 @@ constexpr int kRedChunks = 8;
 // this the reduce runs in two stages: workgroups of kRedBlockRows rows
 // each, then one pass over their sums; with fewer, one pass.
 constexpr int kRedBlockRows = 2048;
+// Backward lanes in column blocks (C / V a multiple of 64 and at least
+// kBlock, bands shorter than kCbMaxRows): a workgroup holds 64 channel
+// vectors of kCbBands consecutive bands, one band per wave, and writes one
+// partial row for them.  Its rows, kCbBands * rows + 6 < 4103, always fit
+// the document-start bitmask.
+constexpr int kCbBands = 4;
+constexpr int kCbMaxRows = 1024;
+inline bool bwd_column_blocks(int64_t nvec, int64_t rows) {
+  return nvec >= kBlock && nvec % 64 == 0 && rows < kCbMaxRows;
+}
+static_assert(kCbBands * kCbMaxRows + 6 < 32 * (kDocMaskWords - 1),
+              "column-block workgroups must fit the document-start bitmask");
 
 // Everything a launch needs, decided on the host from (direction, S, C,
 // policy) alone - never from tensor contents.
@@ -76,7 +88,8 @@ struct Plan {
   int32_t red_blocks;  // reduce workgroups per row range (kRedOut outputs each)
   int32_t red_stage1;  // first-stage row ranges (0: the reduce is one pass)
   int32_t wg_rows;     // backward: 1 = one partial row per workgroup, 0 = per band
-  int32_t prows;       // backward partial rows: blocks (wg_rows) or bands
+  int32_t cb;          // backward: 1 = lanes in column blocks of kCbBands bands
+  int32_t prows;       // backward partial rows: blocks (wg_rows), band groups (cb) or bands
 };
 
 struct FwdArgs {
@@ -114,6 +127,7 @@ struct BwdArgs {
   int32_t bands;
   int32_t blocks;      // workgroups with lanes (the grid may be padded)
   int32_t wg_rows;     // 1: one partial row per workgroup (see Plan)
+  int32_t cb;          // 1: column-block lanes, one partial row per band group
 };
 
 struct ReduceArgs {

@@ -298,15 +298,13 @@ __device__ __forceinline__ int32_t doc_mask_prefetch(const int32_t* cu, int32_t 
 }
 
 // Every thread of the workgroup must call this (two barriers).  The rows
-// touched are the workgroup's bands plus three halo rows on each side; the
+// touched are the workgroup's bands (first_band .. last_band, clamped to the
+// last band by the caller) plus three halo rows on each side; the
 // last band's rows may run past S (and past 2^31 - 1), where no start
 // matters, so only starts below S are marked.
-__device__ __forceinline__ void build_doc_mask(DocMask& m, uint32_t place, int32_t t_pre,
-                                               const int32_t* cu, int32_t num_docs, int32_t S,
-                                               int32_t nvec, int32_t rows, int32_t bands) {
-  const int32_t g0 = (int32_t)place * kBlock;
-  const int32_t first_band = g0 / nvec;
-  const int32_t last_band = min((g0 + kBlock - 1) / nvec, bands - 1);
+__device__ __forceinline__ void build_doc_mask(DocMask& m, int32_t first_band, int32_t last_band,
+                                               int32_t t_pre, const int32_t* cu, int32_t num_docs,
+                                               int32_t S, int32_t rows) {
   const int32_t row_lo = first_band * rows - 3;
   const int64_t row_end = (int64_t)(last_band + 1) * rows + 3;
   // At most kDocMaskWords + 1 words by the host's choice of rows.
@@ -595,6 +593,39 @@ __device__ __forceinline__ bool lane_coords(uint32_t place, int32_t nvec, int32_
   return active;
 }
 
+// Bands of the linear lane map's workgroup `place`: its kBlock lanes.
+__device__ __forceinline__ void linear_bands(uint32_t place, int32_t nvec, int32_t bands,
+                                             int32_t& first, int32_t& last) {
+  const int32_t g0 = (int32_t)place * kBlock;
+  first = g0 / nvec;
+  last = min((g0 + kBlock - 1) / nvec, bands - 1);
+}
+
+// Column-block lanes of the backward (C / V a multiple of 64, at least
+// kBlock): workgroup `place` holds vectors [64 b, 64 b + 64) of bands
+// kCbBands q .. kCbBands q + kCbBands - 1, one band per wave, with
+// q = place / (C / (64 V)) and b the remainder.  A wave reads the same
+// 512 contiguous bytes of each row as under the linear map; the workgroup
+// can then add its bands' totals before writing them.
+template <int V>
+__device__ __forceinline__ bool lane_coords_cb(uint32_t place, int32_t nvec, int32_t rows,
+                                               int32_t bands, int32_t C, Lane& L) {
+  const uint32_t nblk = (uint32_t)nvec / 64u;
+  const uint32_t q = place / nblk;
+  // The wave's band, the same for all its lanes.
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x) / 64u;
+  const uint32_t band = q * (uint32_t)kCbBands + wave;
+  const bool active = band < (uint32_t)bands;
+  // Waves past the last band keep the last band's coordinates (they load
+  // and store nothing), as under the linear map.
+  L.band = active ? band : (uint32_t)bands - 1u;
+  L.vec = active ? (place - q * nblk) * 64u + (threadIdx.x & 63u) : 0u;
+  L.t0 = (int32_t)L.band * rows;
+  L.base_row = max(L.t0 - 3, 0);
+  L.off = (L.t0 - 3 - L.base_row) * (C * 2) + (int32_t)L.vec * (V * 2);
+  return active;
+}
+
 // ===================================================== forward kernel ==
 
 template <bool kBias, int V>
@@ -689,7 +720,11 @@ void fwd_kernel(FwdArgs a) {
                                 3 * (int64_t)row_bytes,
                             row_bytes, threadIdx.x & 63u, L.vec, a.nvec, V * 2);
 
-  build_doc_mask(dmask, place, cu_pre, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
+  {
+    int32_t first, last;
+    linear_bands(place, a.nvec, a.bands, first, last);
+    build_doc_mask(dmask, first, last, cu_pre, a.cu, a.num_docs, a.S, a.rows);
+  }
   if (!active) return;
   float w[4][V], bv[V];
   unpack_params<V>(praw, a.w_bf16, a.b_bf16, w, bv);
@@ -916,7 +951,7 @@ __device__ __forceinline__ void bwd_row(const float (&w)[4][V], const float (&bv
   }
 }
 
-template <bool kBias, bool kBf16Policy, bool kNt, typename Acc, int V>
+template <bool kBias, bool kBf16Policy, bool kNt, bool kCb, typename Acc, int V>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(kBwdWaves)))
 void bwd_main_kernel(BwdArgs a) {
   typedef Vec<V> VT;
@@ -932,7 +967,8 @@ void bwd_main_kernel(BwdArgs a) {
   Lane L;
   const uint32_t place = block_place();
   if (place >= (uint32_t)a.blocks) return;  // padding workgroup: no lane
-  const bool active = lane_coords<V>(place, a.nvec, a.rows, a.bands, a.C, L);
+  const bool active = kCb ? lane_coords_cb<V>(place, a.nvec, a.rows, a.bands, a.C, L)
+                           : lane_coords<V>(place, a.nvec, a.rows, a.bands, a.C, L);
   // Parameters, the SiLU' table and the document starts are requested
   // before the activations: loads complete in issue order, so waiting for
   // these waits for no activation row.
@@ -977,10 +1013,20 @@ void bwd_main_kernel(BwdArgs a) {
   // Every thread stages its part of the SiLU' table (the mask builder's
   // barriers make it visible).
   if (kBf16Policy) lut_stage_store(lut_stage, lut_lds);
-  build_doc_mask(dmask, place, cu_pre, a.cu, a.num_docs, a.S, a.nvec, a.rows, a.bands);
+  {
+    int32_t first, last;
+    if (kCb) {
+      first = (int32_t)(place / ((uint32_t)a.nvec / 64u)) * kCbBands;
+      last = min(first + kCbBands - 1, a.bands - 1);
+    } else {
+      linear_bands(place, a.nvec, a.bands, first, last);
+    }
+    build_doc_mask(dmask, first, last, cu_pre, a.cu, a.num_docs, a.S, a.rows);
+  }
   // Lanes past the last band have nothing to compute; with one partial row
-  // per workgroup they still join its final sum (one barrier).
-  if (!active && !a.wg_rows) return;
+  // per workgroup (or band group) they still join its final sum (one
+  // barrier).
+  if (!active && !a.wg_rows && !kCb) return;
   // Band total j of lane l in LDS: in the lane's own 16-byte column of
   // `stage` (the masked path uses only the thread's own column too, so a
   // thread writing its totals disturbs no thread still in its loop).
@@ -1117,7 +1163,7 @@ void bwd_main_kernel(BwdArgs a) {
   }
   run(xa, da, a.rows, 3, false);
 
-  if (!a.wg_rows) {
+  if (!a.wg_rows && !kCb) {
     // One partial row per band: part[band][k][c].
     Acc* part = reinterpret_cast<Acc*>(a.part) + (int64_t)L.band * 5 * a.C + L.vec * V;
 #pragma unroll
@@ -1137,13 +1183,39 @@ void bwd_main_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 5 * V; ++j) *slot(j, threadIdx.x) = (Acc)0;
   }
-  if (!a.wg_rows) return;
+  if (!a.wg_rows && !kCb) return;
+  __syncthreads();
+
+  if (kCb) {
+    // One partial row per band group: part[q][k][c] for the workgroup's 64
+    // vectors.  Thread t sums lane t of each wave, that is vector t of
+    // bands kCbBands q, kCbBands q + 1, ... in that order, in binary64, and
+    // rounds once to the partial element type (waves past the last band
+    // left zeros).
+    if (threadIdx.x < 64u) {
+      const uint32_t nblk = (uint32_t)a.nvec / 64u;
+      const uint32_t q = place / nblk;
+      const uint32_t vec = (place - q * nblk) * 64u + threadIdx.x;
+      double s[5 * V];
+#pragma unroll
+      for (int j = 0; j < 5 * V; ++j) s[j] = 0.0;
+#pragma unroll
+      for (int w = 0; w < kCbBands; ++w)
+#pragma unroll
+        for (int j = 0; j < 5 * V; ++j) s[j] += (double)*slot(j, threadIdx.x + 64u * w);
+      Acc* part = reinterpret_cast<Acc*>(a.part) + (int64_t)q * 5 * a.C + (int64_t)vec * V;
+#pragma unroll
+      for (int k = 0; k < 5; ++k)
+#pragma unroll
+        for (int i = 0; i < V; ++i) part[(int64_t)k * a.C + i] = (Acc)s[k * V + i];
+    }
+    return;
+  }
 
   // One partial row per workgroup: part[place][k][c].  The workgroup's lanes
   // cover every vector of channels (C/V < kBlock), some twice; thread t sums
   // vector t's lanes in increasing lane order, that is in increasing band
   // order, in binary64, and rounds once to the partial element type.
-  __syncthreads();
   if ((int32_t)threadIdx.x < a.nvec) {
     const uint32_t nvec = (uint32_t)a.nvec;
     const uint32_t first = (threadIdx.x + nvec - (place * (uint32_t)kBlock) % nvec) % nvec;
@@ -1255,10 +1327,16 @@ hipError_t launch_fwd_v(const Plan& plan, const FwdArgs& a, bool has_bias, hipSt
 
 template <bool kBias, bool kBf16Policy, typename Acc, int V>
 void launch_bwd_main_t(dim3 grid, dim3 block, hipStream_t s, const BwdArgs& a) {
-  if (rows_line_aligned(a.C))
-    hipLaunchKernelGGL((bwd_main_kernel<kBias, kBf16Policy, true, Acc, V>), grid, block, 0, s, a);
+  // Column blocks (C a multiple of 256) imply rows of a multiple of 128 bytes.
+  if (a.cb)
+    hipLaunchKernelGGL((bwd_main_kernel<kBias, kBf16Policy, true, true, Acc, V>), grid, block, 0,
+                       s, a);
+  else if (rows_line_aligned(a.C))
+    hipLaunchKernelGGL((bwd_main_kernel<kBias, kBf16Policy, true, false, Acc, V>), grid, block, 0,
+                       s, a);
   else
-    hipLaunchKernelGGL((bwd_main_kernel<kBias, kBf16Policy, false, Acc, V>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((bwd_main_kernel<kBias, kBf16Policy, false, false, Acc, V>), grid, block, 0,
+                       s, a);
 }
 
 template <int V>
