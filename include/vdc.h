@@ -102,8 +102,10 @@ enum vdc_status {
  * serves every route of the direction.  VDC_FWD: the forward keeps no
  * counters and needs no workspace, so the answer is 0 (conv1d_fwd accepts
  * workspace = NULL).  VDC_BWD: room for the FP32 / FP64 partial rows of
- * dweight and dbias (one per band of tokens, or per workgroup of the main
- * kernel when 256 <= C < 1024) for every policy, at this (S, C), plus the
+ * dweight and dbias (one per band of tokens; one per workgroup of the main
+ * kernel when 256 <= C < 1024; one per group of four bands when C is a
+ * multiple of 256, at least 1024, and the bands are shorter than 1024
+ * tokens) for every policy, at this (S, C), plus the
  * FP64 sums of the reduce's first stage when there are more than 2048
  * partial rows; the backward writes every byte it later reads, so the
  * buffer needs no zeroing ([B] Parameters workspace).
@@ -226,7 +228,9 @@ const char *conv1d_status_string(int status);
  * element bytes (0 forward, 4 or 8 backward), reduce-kernel workgroups,
  * reduce chunks, channels per lane, first-stage reduce row ranges (0 when
  * the reduce is one launch), partial rows of the backward (0 forward:
- * one per band, or one per workgroup when 256 <= C < 1024) }.
+ * one per band, per workgroup when 256 <= C < 1024, or per group of four
+ * bands when C is a multiple of 256, at least 1024, with bands shorter
+ * than 1024 tokens) }.
  * Returns a vdc_status.
  */
 int conv1d_plan(int direction, int64_t S, int64_t C, int policy, int64_t out[11]);
