@@ -154,8 +154,9 @@ int conv1d_fwd(const void *x, const void *weight, int w_dtype,
  *            contents irrelevant; must not overlap any other argument.
  *
  * Two launches are enqueued in stream order: the main kernel writes dx and
- * one partial row of dweight / dbias per band of tokens into the workspace
- * (FP32 under VDC_SILU_GRAD_BF16, FP64 under VDC_SILU_GRAD_FP32), and the
+ * partial rows of dweight / dbias into the workspace (one per band of
+ * tokens, workgroup or group of bands, as workspace_bytes describes; FP32
+ * under VDC_SILU_GRAD_BF16, FP64 under VDC_SILU_GRAD_FP32), and the
  * reduce kernel sums the rows in FP64 in a fixed order and rounds once to
  * the output dtype ([B] Description).  With more than 2048 partial rows
  * (long sequences of few channels) the reduce takes two launches: sums of

@@ -81,7 +81,7 @@ static_assert(kCbBands * kCbMaxRows + 6 < 32 * (kDocMaskWords - 1),
 struct Plan {
   int32_t vec;         // channels per lane (V)
   int32_t rows;        // tokens per band (T)
-  int32_t bands;       // ceil(S / T); also the backward's partial rows
+  int32_t bands;       // ceil(S / T)
   int64_t lanes;       // bands * C / V
   int32_t blocks;      // main-kernel workgroups
   int32_t acc_bytes;   // backward partial element: 4 (FP32) or 8 (FP64)
@@ -116,7 +116,7 @@ struct BwdArgs {
   const void* w;
   const void* b;
   const int32_t* cu;
-  void* part;          // [bands][5][C] of FP32 or FP64
+  void* part;          // [P][5][C] of FP32 or FP64 (P = Plan::prows)
   int32_t num_docs;
   int32_t w_bf16;
   int32_t b_bf16;

@@ -13,7 +13,10 @@
 //    band of T consecutive tokens, and walks the band row by row.  Lanes are
 //    numbered (band, vector) -> band * (C/4) + vector, so the 64 lanes of a
 //    wave read 64 consecutive vectors of a row (fully coalesced) and, when
-//    C/4 is not a multiple of 64, simply continue into the next band.
+//    C/4 is not a multiple of 64, simply continue into the next band.  The
+//    backward of short bands with C a multiple of 256 numbers them in
+//    column blocks instead (lane_coords_cb): the same 64 vectors per wave,
+//    four bands per workgroup, so that one partial row covers four bands.
 //  * The kernels run one wave per SIMD and the host picks T so that all
 //    waves fit the machine at once; each wave double-buffers groups of
 //    rows in registers and stores a group's outputs after its last row; the
