@@ -342,8 +342,8 @@ def host_cpu_model():
     return None
 
 
-# Host threads of the all-core oracle leg: the CPU share of a one-GPU machine
-# (whatever os.cpu_count() reports there).
+# Host threads of the all-core oracle leg, at most: the host cores a
+# one-GPU job is given, which os.cpu_count() may overstate on a shared host.
 CPU_THREADS_MAX = 16
 
 
